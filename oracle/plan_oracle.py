@@ -1,0 +1,77 @@
+"""Reference of the integer planning rule (bucket, pad, cost order) -- TEST
+INFRASTRUCTURE ONLY, same import restrictions as ``muon_oracle``.
+
+The pages batch matrices of similar shapes so that the Newton-Schulz recurrence
+of many small matrices runs jointly and amortises kernel dispatch (DMuon
+explainer on gist.science, second section 2.1, "Batching"; section 4 credits
+autotuning and batching with 16% of the speed-up), and they balance work by
+computational cost (DMuon abstract).  The rule below is the library's
+documented contract for that step, written out plainly:
+
+* per matrix: m = min(rows, cols), n = max(rows, cols), transposed = rows > cols
+  (a square matrix is not transposed);
+* precision path: "bf16" when the gradient is bf16, "f32" when it is fp32;
+* tile granularity g: 64 on the f32 path; on the bf16 path 128 when m <= 128,
+  else 256;
+* padded dims m_pad = ceil(m / g) g and n_pad = ceil(n / g) g (zero padding);
+* bucket key = (path, m_pad, n_pad): matrices of similar shape share a bucket;
+* buckets are ordered by their executed cost, the sum over members of
+  4 m_pad^2 n_pad + 2 m_pad^3, descending; ties keep the order in which the
+  bucket key first appears;
+* inside a bucket, members keep their input order (slot 0, 1, ...);
+* the reported per-matrix cost is 4 m^2 n + 2 m^3 of the real shape.
+"""
+
+from __future__ import annotations
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def tile_granularity(path: str, m: int) -> int:
+    if path == "f32":
+        return 64
+    return 128 if m <= 128 else 256
+
+
+def _ceil_to(x: int, g: int) -> int:
+    return -(-x // g) * g
+
+
+def _cost(m: int, n: int) -> int:
+    return 4 * m * m * n + 2 * m * m * m
+
+
+def plan_reference(descs):
+    """descs: list of (rows, cols, grad_dtype, param_dtype) with dtype codes
+    0 = fp32, 1 = bf16.  Returns a list of per-matrix dicts with keys
+    bucket, slot, transposed, m, n, m_pad, n_pad, cost, and the list of
+    buckets (path, m_pad, n_pad, members) in execution order."""
+    items = []
+    keys_in_order = []
+    members = {}
+    for idx, (r, c, gd, _pd) in enumerate(descs):
+        r, c = int(r), int(c)
+        if r <= 0 or c <= 0:
+            raise ValueError("matrix dims must be positive")
+        m, n = min(r, c), max(r, c)
+        path = "bf16" if gd == DTYPE_BF16 else "f32"
+        g = tile_granularity(path, m)
+        key = (path, _ceil_to(m, g), _ceil_to(n, g))
+        if key not in members:
+            members[key] = []
+            keys_in_order.append(key)
+        members[key].append(idx)
+        items.append({"transposed": r > c, "m": m, "n": n, "m_pad": key[1],
+                      "n_pad": key[2], "cost": _cost(m, n), "key": key})
+    first_seen = {k: i for i, k in enumerate(keys_in_order)}
+    order = sorted(keys_in_order,
+                   key=lambda k: (-len(members[k]) * _cost(k[1], k[2]), first_seen[k]))
+    buckets = []
+    for b, key in enumerate(order):
+        for slot, idx in enumerate(members[key]):
+            items[idx]["bucket"] = b
+            items[idx]["slot"] = slot
+        buckets.append({"path": key[0], "m_pad": key[1], "n_pad": key[2],
+                        "members": list(members[key])})
+    return items, buckets
