@@ -1,0 +1,212 @@
+"""Benchmark of the owner-side Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one muon_step_batched call over the whole matrix set: momentum,
+normalisation, 5 quintic Newton-Schulz iterations on the short side and the
+parameter update, with every input already resident in device memory.  The
+default workload is the Llama-3.1-8B projection set's owner share (one of 8 LPT
+owners: 28 matrices, bf16 gradients and parameters, fp32 momentum).
+
+Printed: one JSON line.  ``value`` is the algorithmic Newton-Schulz throughput
+of the whole step, sum over matrices of 5 (m(m+1)n + m(m+1)m + 2 m^2 n) flops
+(the Gram and A A^T triangles plus the dense B X product) divided by the step
+time.  ``roofline`` covers the dominant kernel, the B X product, timed live
+with HIP events at its launch boundaries inside the timed steps.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector/matrix
+NS_STEPS = 5
+LR, BETA, EPS = 0.02, 0.95, 1e-7
+
+
+def algorithmic_flops(m: int, n: int) -> int:
+    """One NS iteration: Gram triangle m(m+1)n, A A^T triangle m(m+1)m, B X 2m^2 n."""
+    return m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n
+
+
+def dense_flops(m: int, n: int) -> int:
+    return 4 * m * m * n + 2 * m * m * m
+
+
+def bx_flops(m: int, n: int) -> int:
+    return 2 * m * m * n
+
+
+def read_traffic(kernel_tag: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (sha256 recorded in the summary)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    src = os.path.join(ROOT, "matrix_optimizer_02_amd", "csrc", "k_gemm_bf16.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, host_samples):
+    """Time the fp64 oracle on a bounded sample of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    flops = 0
+    t0 = time.perf_counter()
+    names = []
+    for i, (g, mm, ww) in host_samples:
+        spec = w.matrices[i]
+        oracle.muon_step(g, mm, ww, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS)
+        m, n = min(spec.rows, spec.cols), max(spec.rows, spec.cols)
+        flops += NS_STEPS * algorithmic_flops(m, n)
+        names.append(f"{spec.name} {spec.rows}x{spec.cols}")
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "full fp64 oracle Muon step on " + ", ".join(names) + f" ({dt:.1f} s)",
+            "seconds": dt}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3.1-8b_owner_1of8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the owner-side step is one GPU's share of the work and this "
+              "build runs no collectives; run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from matrix_optimizer_02_amd import dmuon_ns as d
+    from matrix_optimizer_02_amd.workloads import get_workload, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = get_workload(args.workload)
+    G, M, W = make_inputs(w, dev, seed=args.seed)
+    paths = {s.grad_dtype for s in w.matrices}
+
+    # bounded oracle sample: one matrix per distinct shape, smallest first, up to ~8 TFLOP dense
+    host_samples = []
+    if not args.no_cpu_baseline:
+        seen, budget = set(), 8e12
+        order = sorted(range(w.count), key=lambda i: dense_flops(min(w.matrices[i].rows, w.matrices[i].cols),
+                                                                 max(w.matrices[i].rows, w.matrices[i].cols)))
+        for i in order:
+            s = w.matrices[i]
+            key = (s.rows, s.cols)
+            cost = NS_STEPS * dense_flops(min(s.rows, s.cols), max(s.rows, s.cols))
+            if key in seen or cost > budget:
+                continue
+            seen.add(key)
+            budget -= cost
+            host_samples.append((i, (G[i].double().cpu().numpy(), M[i].double().cpu().numpy(),
+                                     W[i].double().cpu().numpy())))
+
+    plan = d.plan_for(G, [x.dtype for x in W])
+    ws = d.workspace_for(plan, dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
+    events = [d.PhaseEvents(NS_STEPS) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        d.muon_step_batched_profiled(plan, G, M, W, events[k], lr=LR, beta=BETA, eps=EPS,
+                                     workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    names = events[0].names()
+    per = [e.elapsed_ms() for e in events]
+    avg = {nm: sum(p[j] for p in per) / len(per) for j, nm in enumerate(names)}
+    bx_ms = [p[j] for p in per for j, nm in enumerate(names) if nm.startswith("bx")]
+    gemm_ms = [p[j] for p in per for j, nm in enumerate(names) if nm[:-1] in ("gram", "square", "bx")]
+    bx_avg = sum(bx_ms) / len(bx_ms)
+
+    alg = dense = bxf = 0
+    for s in w.matrices:
+        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
+        alg += NS_STEPS * algorithmic_flops(m, n)
+        dense += NS_STEPS * dense_flops(m, n)
+        bxf += bx_flops(m, n)
+    step_s = ms_per_step / 1e3
+    value = alg / step_s / 1e12
+    peak = BF16_PEAK_TFLOPS if paths == {"bf16"} else FP32_PEAK_TFLOPS
+    achieved = bxf / (bx_avg / 1e3) / 1e12
+    traffic = read_traffic("bx_gemm_bf16_llama8b") if args.workload == "llama3.1-8b_owner_1of8" else None
+
+    out = {
+        "metric": "NS TFLOP/s and % bf16 MFMA peak, Muon step ms for Llama-3-8B owner share",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if paths == {"bf16"} else ("f32" if paths == {"f32"} else "bf16+f32"),
+        "data": "synthetic (seeded normal gradients, momenta and parameters)",
+        "config": {"workload": w.name, "matrices": w.count, "elements": w.elements(),
+                   "ns_steps": NS_STEPS, "lr": LR, "beta": BETA, "nesterov": True},
+        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 3),
+        "ns_tflops_dense_equiv": round(dense / step_s / 1e12, 3),
+        "matrices_per_s": round(w.count / step_s, 2),
+        "phase_ms": {k: round(v, 4) for k, v in avg.items()},
+        "gemm_ms_per_step": round(sum(gemm_ms) / len(per), 4),
+        "roofline": {"bound": "mfma", "kernel": "ns_gemm_bf16_kernel<256, BX> (X' = a X + B X)",
+                     "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "launch_ms": round(bx_avg, 4), "flops_per_launch": bxf},
+    }
+    if host_samples:
+        out["cpu_baseline"] = cpu_baseline(w, host_samples)
+    for e in events:
+        e.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * libdmuon_ns -- the owner-side Muon step on one MI355X (gfx950), C ABI.
+ *
+ * What the library computes.  For every matrix of a batch, independently:
+ *   M' = beta M + G;  U = G + beta M' (Nesterov) or U = M';
+ *   X  = U / (||U||_F + eps), taken on the short side (U^T when rows > cols);
+ *   ns_steps times:  A = X X^T;  B = b A + c A A;  X = a X + B X;
+ *   O  = X in the stored orientation;  W' = W (1 - lr wd) - lr s O,
+ *   s  = sqrt(max(1, rows / cols)).
+ * The pages describe this as the work of a matrix's single owner: it runs the
+ * Newton-Schulz (NS) iteration and the optimizer update once, on the full
+ * matrix (DMuon abstract, arXiv 2611.07084 listing; DMuon explainer on
+ * gist.science, "Technische Samenvatting" section 2.1 Owner-Centric
+ * Executiestrategie), on the momentum-aggregated gradient (explainer section 1
+ * Probleemstelling), in the m x m Gram space of the short side with the
+ * symmetric product X X^T computed as one triangle (explainer, second section
+ * 2.1, Efficiente Gram Newton-Schulz Iteratie), with similar shapes batched to
+ * amortise dispatch (same section, "Batching").  The user-facing form on the
+ * pages is dmuon.Muon(model, lr=0.02, ns_steps=5, ...) (DMuon docs, section
+ * "LLM 预训练").  The pages print no coefficients; the workloads use
+ * (a, b, c) = (3.4445, -4.7750, 2.0315), beta = 0.95, lr = 0.02, 5 steps.
+ *
+ * Conventions shared by every entry point.
+ *  - Every function returns a dmuon_status; no C++ exception crosses the ABI.
+ *  - Matrices are dense, row-major, rows x cols, contiguous (leading
+ *    dimension = cols).  Every device pointer must be 16-byte aligned.
+ *  - "Device pointer" = memory of the HIP device current on the calling
+ *    thread; pointer arrays themselves are HOST arrays, in the order of the
+ *    plan's descriptors.
+ *  - The caller owns every device buffer (gradients, momenta, parameters,
+ *    outputs, workspace).  The step entry points allocate no device memory;
+ *    they only enqueue work on `stream` (a hipStream_t, NULL = the default
+ *    stream) and return.  Buffers must stay alive until the stream has passed
+ *    that point.
+ *  - Arguments are checked before anything is enqueued: on an error return
+ *    nothing has been enqueued.  A launch failure returns DMUON_ERR_HIP (work
+ *    enqueued before it may have run).
+ *  - Results are deterministic: same plan, inputs and device give bitwise
+ *    identical outputs (no floating-point atomics).
+ *  - NaN and Inf in the inputs are not masked; they propagate.
+ *  - Calls that share a workspace must not overlap in time; a plan may be
+ *    shared by threads and streams if each call has its own workspace.
+ */
+#ifndef DMUON_NS_H
+#define DMUON_NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DMUON_API __attribute__((visibility("default")))
+#else
+#define DMUON_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DMUON_OK = 0,
+    DMUON_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad dtype, bad index */
+    DMUON_ERR_UNSUPPORTED = -2, /* valid request outside the library's limits (e.g. a dim >= 2^30) */
+    DMUON_ERR_WORKSPACE = -3,   /* workspace missing, too small or not 256-byte aligned */
+    DMUON_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    DMUON_ERR_ALLOC = -5        /* host allocation failed (plan creation) */
+} dmuon_status;
+
+typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype;
+
+/* One matrix of the batch.  grad_dtype selects the precision path: a bf16
+ * gradient runs NS with bf16 MFMA operands and fp32 accumulation; an fp32
+ * gradient runs NS in fp32 throughout.  param_dtype is the dtype of the
+ * parameter (muon_step_batched) or of the output (ns_orthogonalize_batched).
+ * Momentum buffers are always fp32. */
+typedef struct {
+    int64_t rows;        /* stored rows (output features), >= 1 */
+    int64_t cols;        /* stored cols (input features), >= 1 */
+    int32_t grad_dtype;  /* dmuon_dtype */
+    int32_t param_dtype; /* dmuon_dtype */
+} dmuon_matrix_desc;
+
+/* Step hyper-parameters.  ns_steps >= 0 (0: O is the normalised U).
+ * nesterov != 0 selects U = G + beta M'.  eps is added to the Frobenius norm. */
+typedef struct {
+    float lr;
+    float beta;
+    float weight_decay;
+    float eps;
+    float a, b, c;
+    int32_t ns_steps;
+    int32_t nesterov;
+} dmuon_hparams;
+
+typedef struct dmuon_plan dmuon_plan; /* opaque, host memory only, immutable once built */
+
+/* Build the batch plan (host only, no device work).  Per matrix: m = min(rows,
+ * cols), n = max(rows, cols), transposed = rows > cols (square matrices are
+ * not transposed).  Tile granularity g = 64 on the fp32 path; on the bf16 path
+ * g = 128 when m <= 128, else 256.  Padded dims are m, n rounded up to g (the
+ * padding is zero and leaves the result unchanged).  Matrices with the same
+ * (path, padded m, padded n) share a bucket and run jointly.  Buckets are
+ * ordered by executed cost, the sum of 4 m_pad^2 n_pad + 2 m_pad^3 over their
+ * members, descending, ties in order of first appearance; members keep input
+ * order.  count == 0 gives an empty plan.  Errors: INVALID_ARG for count < 0,
+ * descs == NULL with count > 0, out == NULL, a dim < 1 or an unknown dtype;
+ * UNSUPPORTED for a dim >= 2^30; ALLOC on host allocation failure.
+ * On success *out owns the plan; release it with muon_plan_destroy. */
+DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
+
+/* Bytes of device workspace a step or orthogonalisation with this plan needs
+ * (0 for an empty plan).  The workspace holds the per-bucket X, X^T (two
+ * copies), A and B operands, per-matrix norms and a small descriptor table;
+ * its contents need no initialisation and are garbage after a call. */
+DMUON_API dmuon_status muon_plan_workspace_bytes(const dmuon_plan* plan, size_t* bytes);
+
+/* Number of matrices and buckets of the plan. */
+DMUON_API dmuon_status muon_plan_info(const dmuon_plan* plan, int32_t* count, int32_t* num_buckets);
+
+/* Per-matrix plan entry: bucket index (execution order), slot within the
+ * bucket, transposed flag, padded short/long dims, and the dense NS cost
+ * 4 m^2 n + 2 m^3 of the real shape.  Any output pointer may be NULL.
+ * INVALID_ARG for idx outside [0, count). */
+DMUON_API dmuon_status muon_plan_query(const dmuon_plan* plan, int32_t idx, int32_t* bucket, int32_t* slot,
+                             int32_t* transposed, int64_t* padded_m, int64_t* padded_n,
+                             int64_t* ns_cost);
+
+/* Per-bucket plan entry: precision path (dmuon_dtype of its gradients),
+ * padded dims, member count and tile granularity. */
+DMUON_API dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket, int32_t* path,
+                              int64_t* padded_m, int64_t* padded_n, int32_t* count,
+                              int32_t* tile);
+
+/* Release a plan (NULL is a no-op). */
+DMUON_API void muon_plan_destroy(dmuon_plan* plan);
+
+/* One fused Muon step over every matrix of the plan: momentum (in place in
+ * momenta[i], fp32), normalisation, ns_steps NS iterations on the short side,
+ * and the in-place parameter update of params[i] (param_dtype; bf16 results
+ * are rounded to nearest even once, from fp32).
+ *   grads[i]   device, rows x cols, grad_dtype, read only, must not alias
+ *   momenta[i] device, rows x cols, fp32, read and written
+ *   params[i]  device, rows x cols, param_dtype, read and written
+ *   hp         host, step hyper-parameters (ns_steps >= 0)
+ *   workspace  device, >= muon_plan_workspace_bytes, 256-byte aligned
+ *   stream     hipStream_t (NULL = default stream)
+ * Errors: INVALID_ARG (null plan/hp/array/pointer, misaligned pointer,
+ * ns_steps < 0), WORKSPACE, HIP. */
+DMUON_API dmuon_status muon_step_batched(const dmuon_plan* plan, const void* const* grads,
+                               float* const* momenta, void* const* params,
+                               const dmuon_hparams* hp, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Orthogonalise every matrix of the plan without momentum or update:
+ * outputs[i] = NS(inputs[i]) with ns_steps iterations of coefficients
+ * (a, b, c) after normalisation by ||input||_F + eps, in the input's own
+ * orientation.  inputs[i] are device rows x cols in grad_dtype (read only);
+ * outputs[i] are device rows x cols in param_dtype and must not alias the
+ * inputs.  Errors as for muon_step_batched. */
+DMUON_API dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const void* const* inputs,
+                                      void* const* outputs, int32_t ns_steps, float a, float b,
+                                      float c, float eps, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* ---- profiling ------------------------------------------------------------
+ * The step of muon_step_batched, with a HIP event recorded on `stream` at each
+ * phase boundary so that the caller can time every kernel phase live:
+ * events[0] before the first launch, then one event after each phase, the
+ * phases being: prep (momentum, cast, norms), then for every iteration the
+ * Gram, square and BX products (each one grouped launch per tile class), then
+ * the update.  Needs num_events >= muon_step_event_count(hp->ns_steps)
+ * event handles (hipEvent_t, e.g. from dmuon_events_create); nothing is
+ * synchronised.  Errors as for muon_step_batched, INVALID_ARG for too few or
+ * NULL events. */
+DMUON_API dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const void* const* grads,
+                                                  float* const* momenta, void* const* params,
+                                                  const dmuon_hparams* hp, void* workspace,
+                                                  size_t workspace_bytes, void* stream,
+                                                  void* const* events, int32_t num_events);
+
+/* Events muon_step_batched_profiled records: 3 + 3 ns_steps (-1 if ns_steps < 0). */
+DMUON_API int32_t muon_step_event_count(int32_t ns_steps);
+
+/* Create n HIP events (timing enabled) into events[0..n); the caller destroys
+ * them with dmuon_events_destroy.  HIP on failure (none is left created). */
+DMUON_API dmuon_status dmuon_events_create(int32_t n, void** events);
+
+/* Milliseconds between two recorded events; waits for `stop` to complete. */
+DMUON_API dmuon_status dmuon_events_elapsed_ms(void* start, void* stop, float* ms);
+
+/* Destroy n events created by dmuon_events_create (NULL entries skipped). */
+DMUON_API dmuon_status dmuon_events_destroy(int32_t n, void** events);
+
+/* Static, human-readable name of a status code. */
+DMUON_API const char* dmuon_status_string(dmuon_status status);
+
+/* Library version, "major.minor.patch". */
+DMUON_API const char* dmuon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_NS_H */

@@ -1,0 +1,277 @@
+// C-ABI entry points of libdmuon_ns that enqueue device work: argument checks,
+// the per-call matrix table, and the launch sequence of one step
+//   records -> prep (momentum, U, X, X^T, norm partials) -> norms
+//   -> ns_steps x (Gram, square, BX), each one grouped launch per tile class
+//   -> apply (update or output).
+// No device memory is allocated and nothing is synchronised: everything is
+// enqueued on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "dmuon_internal.h"
+#include "launch.h"
+
+using namespace dmuon;
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct StepParams {
+    const void* const* src;
+    float* const* mom;     // nullptr: orthogonalisation
+    void* const* dst;
+    int update;
+    float lr, beta, wd, eps, a, b, c;
+    int ns_steps, nesterov;
+};
+
+dmuon_status check_common(const dmuon_plan* plan, const void* const* src, const void* const* dst,
+                          void* workspace, size_t workspace_bytes) {
+    if (plan == nullptr) return DMUON_ERR_INVALID_ARG;
+    const size_t count = plan->mats.size();
+    if (count == 0) return DMUON_OK;
+    if (src == nullptr || dst == nullptr) return DMUON_ERR_INVALID_ARG;
+    for (size_t i = 0; i < count; ++i) {
+        if (!aligned16(src[i]) || !aligned16(dst[i])) return DMUON_ERR_INVALID_ARG;
+        if (src[i] == dst[i]) return DMUON_ERR_INVALID_ARG;
+    }
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0 ||
+        workspace_bytes < plan->workspace_bytes)
+        return DMUON_ERR_WORKSPACE;
+    return DMUON_OK;
+}
+
+struct TileClass {
+    int path;
+    int tile;
+};
+constexpr TileClass kClasses[] = {{kPathBF16, 256}, {kPathBF16, 128}, {kPathF32, 64}};
+
+hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const StepParams& sp,
+                        int iter, int phase, hipStream_t stream) {
+    for (const TileClass& tc : kClasses) {
+        GemmArgs ga{};
+        ga.ws = ws;
+        ga.scale = scale;
+        ga.a = sp.a;
+        ga.b = sp.b;
+        ga.c = sp.c;
+        ga.phase = phase;
+        ga.first_iter = iter == 0 ? 1 : 0;
+        auto flush = [&]() -> hipError_t {
+            if (ga.nseg == 0) return hipSuccess;
+            hipError_t e = tc.path == kPathBF16 ? launch_gemm_bf16(tc.tile, ga, stream)
+                                                : launch_gemm_f32(ga, stream);
+            ga.nseg = 0;
+            ga.total_blocks = 0;
+            return e;
+        };
+        for (const BucketPlan& bp : p->buckets) {
+            if (bp.path != tc.path || bp.tile != tc.tile) continue;
+            if (ga.nseg == kMaxSeg) {
+                hipError_t e = flush();
+                if (e != hipSuccess) return e;
+            }
+            GemmSeg& s = ga.seg[ga.nseg++];
+            s.tm = (int32_t)(bp.m_pad / bp.tile);
+            s.tn = (int32_t)(bp.n_pad / bp.tile);
+            s.tiles_per_mat = phase == kBX ? s.tm * s.tn : s.tm * (s.tm + 1) / 2;
+            s.count = (int32_t)bp.members.size();
+            s.plan_base = bp.plan_base;
+            s.first_block = ga.total_blocks;
+            s.m_pad = bp.m_pad;
+            s.n_pad = bp.n_pad;
+            s.x_off = (int64_t)bp.off_x;
+            s.xt_src_off = (int64_t)(iter % 2 == 0 ? bp.off_xt0 : bp.off_xt1);
+            s.xt_dst_off = (int64_t)(iter % 2 == 0 ? bp.off_xt1 : bp.off_xt0);
+            s.a_off = (int64_t)bp.off_a;
+            s.b_off = (int64_t)bp.off_b;
+            s.x_stride = bp.m_pad * bp.n_pad * bp.esize;
+            s.a_stride = bp.m_pad * bp.m_pad * bp.esize;
+            ga.total_blocks += s.count * s.tiles_per_mat;
+        }
+        hipError_t e = flush();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// events == nullptr: plain run.  Otherwise events[0] is recorded before the
+// first launch and events[1 + k] after phase k, phases being: prep (records,
+// momentum/cast, norms), then per iteration Gram, square, BX, then apply.
+dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
+                 void* const* events = nullptr) {
+    const int32_t count = (int32_t)p->mats.size();
+    if (count == 0) return DMUON_OK;
+    int ev = 0;
+    auto mark = [&]() -> bool {
+        if (events == nullptr) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(events[ev++]), stream) == hipSuccess;
+    };
+    if (!mark()) return DMUON_ERR_HIP;
+    char* ws = static_cast<char*>(workspace);
+    DevMatRec* table = reinterpret_cast<DevMatRec*>(ws + p->off_records);
+    float* scale = reinterpret_cast<float*>(ws + p->off_scale);
+    float* partials = reinterpret_cast<float*>(ws + p->off_partials);
+
+    // per-matrix records, plan order, written into the workspace by small launches
+    RecChunk chunk{};
+    chunk.table = table;
+    int64_t prep_blocks = 0, apply_blocks = 0;
+    for (int32_t pi = 0; pi < count; ++pi) {
+        const int32_t in = p->order[pi];
+        const MatPlan& mp = p->mats[in];
+        const BucketPlan& bp = p->buckets[mp.bucket];
+        const int64_t xsz = bp.m_pad * bp.n_pad * bp.esize;
+        DevMatRec r{};
+        r.src = sp.src[in];
+        r.mom = sp.mom ? sp.mom[in] : nullptr;
+        r.dst = sp.dst[in];
+        r.x_off = (int64_t)bp.off_x + mp.slot * xsz;
+        r.xt_off0 = (int64_t)bp.off_xt0 + mp.slot * xsz;
+        r.xt_off1 = (int64_t)bp.off_xt1 + mp.slot * xsz;
+        r.partial_off = mp.partial_off;
+        r.prep_begin = prep_blocks;
+        prep_blocks += mp.prep_tiles;
+        r.apply_begin = apply_blocks;
+        apply_blocks += ((mp.rows + kPrepTile - 1) / kPrepTile) * ((mp.cols + kPrepTile - 1) / kPrepTile);
+        r.rows = (int32_t)mp.rows;
+        r.cols = (int32_t)mp.cols;
+        r.r_pad = (int32_t)mp.r_pad;
+        r.c_pad = (int32_t)mp.c_pad;
+        r.transposed = mp.transposed;
+        r.src_dtype = mp.grad_dtype;
+        r.dst_dtype = mp.param_dtype;
+        r.path = bp.path;
+        r.upd_scale = (float)std::sqrt(std::max(1.0, (double)mp.rows / (double)mp.cols));
+        chunk.rec[chunk.n++] = r;
+        if (chunk.n == kRecChunk || pi == count - 1) {
+            if (launch_write_records(chunk, stream) != hipSuccess) return DMUON_ERR_HIP;
+            chunk.first += chunk.n;
+            chunk.n = 0;
+        }
+    }
+
+    PrepArgs pa{};
+    pa.recs = table;
+    pa.count = count;
+    pa.ws = ws;
+    pa.partials = partials;
+    pa.beta = sp.beta;
+    pa.nesterov = sp.nesterov ? 1 : 0;
+    pa.has_momentum = sp.mom ? 1 : 0;
+    pa.total_blocks = prep_blocks;
+    if (launch_prep(pa, stream) != hipSuccess) return DMUON_ERR_HIP;
+    if (launch_finalize_norms(table, count, partials, scale, sp.eps, stream) != hipSuccess)
+        return DMUON_ERR_HIP;
+    if (!mark()) return DMUON_ERR_HIP;
+
+    for (int it = 0; it < sp.ns_steps; ++it)
+        for (int phase : {kGram, kSquare, kBX}) {
+            if (launch_phase(p, ws, scale, sp, it, phase, stream) != hipSuccess) return DMUON_ERR_HIP;
+            if (!mark()) return DMUON_ERR_HIP;
+        }
+
+    ApplyArgs aa{};
+    aa.recs = table;
+    aa.count = count;
+    aa.ws = ws;
+    aa.scale = scale;
+    aa.final_copy = sp.ns_steps % 2;
+    aa.use_scale = sp.ns_steps == 0 ? 1 : 0;
+    aa.update = sp.update;
+    aa.lr = sp.lr;
+    aa.weight_decay = sp.wd;
+    aa.total_blocks = apply_blocks;
+    if (launch_apply(aa, stream) != hipSuccess) return DMUON_ERR_HIP;
+    if (!mark()) return DMUON_ERR_HIP;
+    return DMUON_OK;
+}
+
+}  // namespace
+
+extern "C" dmuon_status muon_step_batched(const dmuon_plan* plan, const void* const* grads,
+                                          float* const* momenta, void* const* params,
+                                          const dmuon_hparams* hp, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    if (plan == nullptr || hp == nullptr || hp->ns_steps < 0) return DMUON_ERR_INVALID_ARG;
+    dmuon_status st = check_common(plan, grads, params, workspace, workspace_bytes);
+    if (st != DMUON_OK || plan->mats.empty()) return st;
+    if (momenta == nullptr) return DMUON_ERR_INVALID_ARG;
+    for (size_t i = 0; i < plan->mats.size(); ++i) {
+        if (!aligned16(momenta[i])) return DMUON_ERR_INVALID_ARG;
+        if (momenta[i] == grads[i] || momenta[i] == params[i]) return DMUON_ERR_INVALID_ARG;
+    }
+    StepParams sp{grads, momenta, params, 1, hp->lr, hp->beta, hp->weight_decay, hp->eps,
+                  hp->a, hp->b, hp->c, hp->ns_steps, hp->nesterov};
+    return run(plan, sp, workspace, static_cast<hipStream_t>(stream));
+}
+
+extern "C" dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const void* const* inputs,
+                                                 void* const* outputs, int32_t ns_steps, float a,
+                                                 float b, float c, float eps, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+    if (plan == nullptr || ns_steps < 0) return DMUON_ERR_INVALID_ARG;
+    dmuon_status st = check_common(plan, inputs, outputs, workspace, workspace_bytes);
+    if (st != DMUON_OK || plan->mats.empty()) return st;
+    StepParams sp{inputs, nullptr, outputs, 0, 0.f, 0.f, 0.f, eps, a, b, c, ns_steps, 0};
+    return run(plan, sp, workspace, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t muon_step_event_count(int32_t ns_steps) {
+    return ns_steps < 0 ? -1 : 3 + 3 * ns_steps;
+}
+
+extern "C" dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const void* const* grads,
+                                                   float* const* momenta, void* const* params,
+                                                   const dmuon_hparams* hp, void* workspace,
+                                                   size_t workspace_bytes, void* stream,
+                                                   void* const* events, int32_t num_events) {
+    if (plan == nullptr || hp == nullptr || hp->ns_steps < 0 || events == nullptr ||
+        num_events < muon_step_event_count(hp->ns_steps))
+        return DMUON_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < num_events; ++i)
+        if (events[i] == nullptr) return DMUON_ERR_INVALID_ARG;
+    dmuon_status st = check_common(plan, grads, params, workspace, workspace_bytes);
+    if (st != DMUON_OK || plan->mats.empty()) return st;
+    if (momenta == nullptr) return DMUON_ERR_INVALID_ARG;
+    for (size_t i = 0; i < plan->mats.size(); ++i) {
+        if (!aligned16(momenta[i])) return DMUON_ERR_INVALID_ARG;
+        if (momenta[i] == grads[i] || momenta[i] == params[i]) return DMUON_ERR_INVALID_ARG;
+    }
+    StepParams sp{grads, momenta, params, 1, hp->lr, hp->beta, hp->weight_decay, hp->eps,
+                  hp->a, hp->b, hp->c, hp->ns_steps, hp->nesterov};
+    return run(plan, sp, workspace, static_cast<hipStream_t>(stream), events);
+}
+
+extern "C" dmuon_status dmuon_events_create(int32_t n, void** events) {
+    if (n < 0 || (n > 0 && events == nullptr)) return DMUON_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (int32_t j = 0; j < i; ++j) (void)hipEventDestroy(static_cast<hipEvent_t>(events[j]));
+            return DMUON_ERR_HIP;
+        }
+        events[i] = e;
+    }
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status dmuon_events_elapsed_ms(void* start, void* stop, float* ms) {
+    if (start == nullptr || stop == nullptr || ms == nullptr) return DMUON_ERR_INVALID_ARG;
+    if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return DMUON_ERR_HIP;
+    if (hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) != hipSuccess)
+        return DMUON_ERR_HIP;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status dmuon_events_destroy(int32_t n, void** events) {
+    if (n < 0 || (n > 0 && events == nullptr)) return DMUON_ERR_INVALID_ARG;
+    dmuon_status st = DMUON_OK;
+    for (int32_t i = 0; i < n; ++i)
+        if (events[i] != nullptr && hipEventDestroy(static_cast<hipEvent_t>(events[i])) != hipSuccess)
+            st = DMUON_ERR_HIP;
+    return st;
+}

@@ -1,0 +1,87 @@
+// Internal types shared by the planner (host C++) and the HIP launchers.
+// Nothing here is part of the C ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/dmuon_ns.h"
+
+namespace dmuon {
+
+constexpr int kPathF32 = DMUON_F32;
+constexpr int kPathBF16 = DMUON_BF16;
+
+// Elementwise kernels work on 64 x 64 tiles of the padded stored-orientation
+// matrix; every tile granularity is a multiple of 64.
+constexpr int kPrepTile = 64;
+constexpr std::size_t kAlign = 256;
+
+inline std::size_t align_up(std::size_t x, std::size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct MatPlan {
+    int64_t rows, cols;
+    int32_t grad_dtype, param_dtype;
+    int64_t m, n;          // short, long side
+    int32_t transposed;    // rows > cols
+    int32_t bucket, slot;  // bucket in execution order, slot inside it
+    int32_t plan_index;    // position in bucket-major execution order
+    int64_t m_pad, n_pad;
+    int64_t cost;          // 4 m^2 n + 2 m^3 of the real shape
+    int64_t r_pad, c_pad;  // padded dims in the stored orientation
+    int64_t prep_tiles;    // 64x64 tiles of the padded stored-orientation grid
+    int64_t partial_off;   // first norm partial of this matrix
+};
+
+struct BucketPlan {
+    int32_t path;          // kPathF32 | kPathBF16
+    int32_t tile;          // tile granularity g
+    int64_t m_pad, n_pad;
+    std::vector<int32_t> members;  // input indices, slot order
+    int32_t plan_base;     // plan index of slot 0
+    int64_t exec_cost;     // count * (4 m_pad^2 n_pad + 2 m_pad^3)
+    int32_t esize;         // bytes per element of X / A / B
+    // byte offsets of the bucket's arrays in the workspace; slot s of array Y
+    // starts at off_Y + s * (its per-matrix size)
+    std::size_t off_x, off_xt0, off_xt1, off_a, off_b;
+};
+
+}  // namespace dmuon
+
+struct dmuon_plan {
+    std::vector<dmuon::MatPlan> mats;        // input order
+    std::vector<dmuon::BucketPlan> buckets;  // execution order
+    std::vector<int32_t> order;              // plan index -> input index
+    int64_t total_prep_tiles = 0;
+    std::size_t off_records = 0, off_scale = 0, off_partials = 0;
+    std::size_t workspace_bytes = 0;
+};
+
+namespace dmuon {
+
+// Per-matrix record kept in the workspace (device side), written at the start
+// of every call.  Indexed by plan index.
+struct DevMatRec {
+    const void* src;       // gradient (step) or input (orthogonalisation)
+    float* mom;            // momentum, nullptr for orthogonalisation
+    void* dst;             // parameter (step) or output (orthogonalisation)
+    int64_t x_off;         // byte offset of this matrix's X in the workspace
+    int64_t xt_off0;       // ... of X^T copy 0
+    int64_t xt_off1;       // ... of X^T copy 1
+    int64_t partial_off;   // first norm partial
+    int64_t prep_begin;    // first prep block of this matrix (prefix sum)
+    int64_t apply_begin;   // first apply block of this matrix (prefix sum)
+    int32_t rows, cols;
+    int32_t r_pad, c_pad;  // padded stored-orientation dims
+    int32_t transposed;
+    int32_t src_dtype, dst_dtype, path;
+    float upd_scale;       // sqrt(max(1, rows / cols))
+    int32_t pad_;
+};
+
+// Apply kernel: each block covers kApplyElems elements of the real matrix.
+constexpr int kApplyThreads = 256;
+constexpr int kApplyElems = kApplyThreads * 8;
+
+}  // namespace dmuon

@@ -1,0 +1,148 @@
+// The three Newton-Schulz products in fp32 (the path taken for fp32
+// gradients), same grouped launches, tile decode and epilogues as the bf16
+// MFMA kernels: Gram A = s X X^T and square B = b A + c A A^T on upper-triangle
+// tiles with mirrored stores, X'^T = s (a X^T + X^T B^T) stored in both
+// orientations.  Products are computed with fp32 FMA on 64 x 64 tiles,
+// 256 threads, 4 x 4 outputs per thread, K staged through LDS 16 at a time.
+//
+// Page basis: as for the bf16 kernels -- X X^T on the full matrix, one
+// triangle of the symmetric products (DMuon explainer on gist.science, second
+// section 2.1 Efficiente Gram Newton-Schulz Iteratie).
+#include "kcommon.h"
+#include "launch.h"
+
+namespace dmuon {
+namespace {
+
+constexpr int kT = 64;
+constexpr int kBKf = 16;
+
+__device__ __forceinline__ void tri_decode_f(int t, int tm, int& I, int& J) {
+    int i = 0;
+    while (t >= tm - i) {
+        t -= tm - i;
+        ++i;
+    }
+    I = i;
+    J = i + t;
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
+    __shared__ float Ps[kBKf][kT + 4];
+    __shared__ float Qs[kBKf][kT + 4];
+
+    const int bid = blockIdx.x;
+    int s = 0;
+    for (int i = 1; i < args.nseg; ++i)
+        if (bid >= args.seg[i].first_block) s = i;
+    const GemmSeg& sg = args.seg[s];
+    const int local = bid - sg.first_block;
+    const int slot = local / sg.tiles_per_mat;
+    const int t = local - slot * sg.tiles_per_mat;
+    const int plan_idx = sg.plan_base + slot;
+
+    int I, J;
+    const float *P, *Q;
+    int64_t ldk, K;
+    if (PHASE == kBX) {
+        I = t / sg.tm;
+        J = t - I * sg.tm;
+        P = reinterpret_cast<const float*>(args.ws + sg.xt_src_off + slot * sg.x_stride);
+        Q = reinterpret_cast<const float*>(args.ws + sg.b_off + slot * sg.a_stride);
+        ldk = sg.m_pad;
+        K = sg.m_pad;
+    } else {
+        tri_decode_f(t, sg.tm, I, J);
+        const int64_t off = PHASE == kGram ? sg.x_off + slot * sg.x_stride : sg.a_off + slot * sg.a_stride;
+        P = Q = reinterpret_cast<const float*>(args.ws + off);
+        ldk = PHASE == kGram ? sg.n_pad : sg.m_pad;
+        K = ldk;
+    }
+    const float* Pt = P + (int64_t)I * kT * ldk;
+    const float* Qt = Q + (int64_t)J * kT * ldk;
+
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int lrow = tid >> 2, lk = (tid & 3) * 4;
+    float acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < K; k0 += kBKf) {
+        const float4 pv = *reinterpret_cast<const float4*>(Pt + lrow * ldk + k0 + lk);
+        const float4 qv = *reinterpret_cast<const float4*>(Qt + lrow * ldk + k0 + lk);
+        Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
+        Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
+        __syncthreads();
+        #pragma unroll
+        for (int k = 0; k < kBKf; ++k) {
+            const float4 av = *reinterpret_cast<const float4*>(&Ps[k][ty * 4]);
+            const float4 bv = *reinterpret_cast<const float4*>(&Qs[k][tx * 4]);
+            const float ar[4] = {av.x, av.y, av.z, av.w};
+            const float br[4] = {bv.x, bv.y, bv.z, bv.w};
+            #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                #pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+    // thread owns rows ty*4 + i and columns tx*4 + j of the 64 x 64 tile
+    const float first_scale = args.first_iter ? args.scale[plan_idx] : 1.0f;
+    const int64_t r0 = (int64_t)I * kT + ty * 4, c0 = (int64_t)J * kT + tx * 4;
+    if (PHASE == kBX) {
+        const int64_t ldm = sg.m_pad, ldn = sg.n_pad;
+        const float* XTs = P;
+        float* XTd = reinterpret_cast<float*>(args.ws + sg.xt_dst_off + slot * sg.x_stride);
+        float* X = reinterpret_cast<float*>(args.ws + sg.x_off + slot * sg.x_stride);
+        float o[4][4];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 xs = *reinterpret_cast<const float4*>(XTs + (r0 + i) * ldm + c0);
+            const float xr[4] = {xs.x, xs.y, xs.z, xs.w};
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) o[i][j] = first_scale * fmaf(args.a, xr[j], acc[i][j]);
+            *reinterpret_cast<float4*>(XTd + (r0 + i) * ldm + c0) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+        }
+        #pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(X + (c0 + j) * ldn + r0) = make_float4(o[0][j], o[1][j], o[2][j], o[3][j]);
+    } else {
+        const int64_t ld = sg.m_pad;
+        const int64_t out_off = PHASE == kGram ? sg.a_off + slot * sg.a_stride : sg.b_off + slot * sg.a_stride;
+        float* Out = reinterpret_cast<float*>(args.ws + out_off);
+        const float alpha = PHASE == kGram ? first_scale * first_scale : args.c;
+        float o[4][4];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 ain = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (PHASE == kSquare) ain = *reinterpret_cast<const float4*>(P + (r0 + i) * ld + c0);
+            const float ar[4] = {ain.x, ain.y, ain.z, ain.w};
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float val = alpha * acc[i][j];
+                if (PHASE == kSquare) val = fmaf(args.b, ar[j], val);
+                o[i][j] = val;
+            }
+            *reinterpret_cast<float4*>(Out + (r0 + i) * ld + c0) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+        }
+        if (I != J) {
+            #pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4*>(Out + (c0 + j) * ld + r0) = make_float4(o[0][j], o[1][j], o[2][j], o[3][j]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream) {
+    if (a.total_blocks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)a.total_blocks), block(256);
+    switch (a.phase) {
+        case kGram: hipLaunchKernelGGL(ns_gemm_f32_kernel<kGram>, grid, block, 0, stream, a); break;
+        case kSquare: hipLaunchKernelGGL(ns_gemm_f32_kernel<kSquare>, grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(ns_gemm_f32_kernel<kBX>, grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dmuon

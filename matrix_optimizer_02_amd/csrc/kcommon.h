@@ -1,0 +1,77 @@
+// Device helpers shared by the HIP kernels of libdmuon_ns (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dmuon_internal.h"
+
+namespace dmuon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32.  bf16 is the upper half of an fp32 bit pattern; the
+// conversion down rounds to nearest even (gfx950 has a hardware instruction
+// for it, which the compiler selects for __bf16 conversions).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static __forceinline__ float load(const float* p) { return *p; }
+    __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ static __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Four consecutive elements <-> float4 (aligned to 4 elements).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(uint16_t* p, float4 v) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    u.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+}
+
+// Largest i in [0, n) with key(i) <= x, for a non-decreasing key (key(0) <= x).
+template <typename F>
+__device__ __forceinline__ int upper_index(int n, int64_t x, F key) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (key(mid) <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Deterministic block sum of one float per thread (fixed reduction tree).
+template <int THREADS>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float total = 0.f;
+    #pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) total += red[w];
+    __syncthreads();
+    return total;
+}
+
+}  // namespace dmuon

@@ -1,0 +1,84 @@
+// Host-side launchers of the HIP kernels (internal to libdmuon_ns).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "dmuon_internal.h"
+
+namespace dmuon {
+
+// ---- elementwise passes (k_elementwise.hip) ----------------------------------
+
+constexpr int kRecChunk = 24;  // records carried by one table-writing launch
+
+struct RecChunk {
+    DevMatRec* table;
+    int32_t first;
+    int32_t n;
+    DevMatRec rec[kRecChunk];
+};
+
+hipError_t launch_write_records(const RecChunk& chunk, hipStream_t stream);
+
+struct PrepArgs {
+    const DevMatRec* recs;
+    int32_t count;
+    char* ws;
+    float* partials;
+    float beta;
+    int32_t nesterov;
+    int32_t has_momentum;  // 0: orthogonalisation (U = input)
+    int64_t total_blocks;
+};
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+
+hipError_t launch_finalize_norms(const DevMatRec* recs, int32_t count, const float* partials,
+                                 float* scale, float eps, hipStream_t stream);
+
+struct ApplyArgs {
+    const DevMatRec* recs;
+    int32_t count;
+    const char* ws;
+    const float* scale;
+    int32_t final_copy;    // which X^T copy holds the result (ns_steps % 2)
+    int32_t use_scale;     // ns_steps == 0: multiply by 1 / (||U|| + eps)
+    int32_t update;        // 1: W' = W (1 - lr wd) - lr s O ; 0: dst = O
+    float lr;
+    float weight_decay;
+    int64_t total_blocks;
+};
+hipError_t launch_apply(const ApplyArgs& a, hipStream_t stream);
+
+// ---- Newton-Schulz products (k_gemm_bf16.hip, k_gemm_f32.hip) ---------------
+
+enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
+constexpr int kMaxSeg = 24;
+
+// One bucket's share of a grouped launch.
+struct GemmSeg {
+    int32_t first_block;    // first block id of this segment in the launch
+    int32_t tiles_per_mat;  // output tiles per matrix
+    int32_t tm;             // tiles along the short side (m_pad / tile)
+    int32_t tn;             // tiles along the long side (n_pad / tile)
+    int32_t count;          // matrices in the bucket
+    int32_t plan_base;      // plan index of slot 0
+    int64_t m_pad, n_pad;
+    int64_t x_off, xt_src_off, xt_dst_off, a_off, b_off;  // bucket base byte offsets
+    int64_t x_stride, a_stride;                           // per-slot bytes
+};
+
+struct GemmArgs {
+    char* ws;
+    const float* scale;  // per plan index: 1 / (||U|| + eps)
+    float a, b, c;
+    int32_t phase;
+    int32_t first_iter;  // apply the normalisation scale in this iteration's epilogues
+    int32_t nseg;
+    int32_t total_blocks;
+    GemmSeg seg[kMaxSeg];
+};
+
+hipError_t launch_gemm_bf16(int tile, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace dmuon

@@ -1,0 +1,200 @@
+// Batch planner: buckets matrices of similar shape, pads them to the tile
+// granularity, orders the work by computational cost and lays out the
+// workspace.  Host-only C++, no device work.
+//
+// Page basis: matrices with similar shapes are batched and their
+// Newton-Schulz recurrence runs jointly, amortising kernel dispatch over many
+// small matrices (DMuon explainer on gist.science, second section 2.1,
+// "Batching"; section 4 credits autotuning and batching with 16% of the
+// speed-up); work is balanced by computational cost (DMuon abstract).  The
+// cost of one iteration on an m x n matrix (m <= n) is taken as
+// 4 m^2 n + 2 m^3: the products X X^T, A A and B X.
+#include <algorithm>
+#include <map>
+#include <new>
+#include <tuple>
+
+#include "dmuon_internal.h"
+
+using namespace dmuon;
+
+namespace {
+
+int64_t ceil_to(int64_t x, int64_t g) { return (x + g - 1) / g * g; }
+
+int64_t dense_cost(int64_t m, int64_t n) { return 4 * m * m * n + 2 * m * m * m; }
+
+int32_t tile_granularity(int32_t path, int64_t m) {
+    if (path == kPathF32) return 64;
+    return m <= 128 ? 128 : 256;
+}
+
+bool valid_dtype(int32_t d) { return d == DMUON_F32 || d == DMUON_BF16; }
+
+}  // namespace
+
+extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out) {
+    if (out == nullptr || count < 0 || (count > 0 && descs == nullptr)) return DMUON_ERR_INVALID_ARG;
+    *out = nullptr;
+    for (int32_t i = 0; i < count; ++i) {
+        const dmuon_matrix_desc& d = descs[i];
+        if (d.rows < 1 || d.cols < 1 || !valid_dtype(d.grad_dtype) || !valid_dtype(d.param_dtype))
+            return DMUON_ERR_INVALID_ARG;
+        if (d.rows >= (int64_t(1) << 30) || d.cols >= (int64_t(1) << 30)) return DMUON_ERR_UNSUPPORTED;
+    }
+    dmuon_plan* p = new (std::nothrow) dmuon_plan();
+    if (p == nullptr) return DMUON_ERR_ALLOC;
+    try {
+        p->mats.resize(count);
+        // bucket key -> bucket under construction (first-appearance index kept)
+        std::map<std::tuple<int32_t, int64_t, int64_t>, int32_t> key_to_tmp;
+        std::vector<BucketPlan> tmp;
+        for (int32_t i = 0; i < count; ++i) {
+            const dmuon_matrix_desc& d = descs[i];
+            MatPlan& mp = p->mats[i];
+            mp.rows = d.rows;
+            mp.cols = d.cols;
+            mp.grad_dtype = d.grad_dtype;
+            mp.param_dtype = d.param_dtype;
+            mp.m = std::min(d.rows, d.cols);
+            mp.n = std::max(d.rows, d.cols);
+            mp.transposed = d.rows > d.cols ? 1 : 0;
+            mp.cost = dense_cost(mp.m, mp.n);
+            const int32_t path = d.grad_dtype;  // the gradient dtype selects the path
+            const int32_t g = tile_granularity(path, mp.m);
+            mp.m_pad = ceil_to(mp.m, g);
+            mp.n_pad = ceil_to(mp.n, g);
+            mp.r_pad = mp.transposed ? mp.n_pad : mp.m_pad;
+            mp.c_pad = mp.transposed ? mp.m_pad : mp.n_pad;
+            mp.prep_tiles = (mp.r_pad / kPrepTile) * (mp.c_pad / kPrepTile);
+            auto key = std::make_tuple(path, mp.m_pad, mp.n_pad);
+            auto it = key_to_tmp.find(key);
+            int32_t b;
+            if (it == key_to_tmp.end()) {
+                b = (int32_t)tmp.size();
+                key_to_tmp.emplace(key, b);
+                BucketPlan bp{};
+                bp.path = path;
+                bp.tile = g;
+                bp.m_pad = mp.m_pad;
+                bp.n_pad = mp.n_pad;
+                bp.esize = path == kPathBF16 ? 2 : 4;
+                tmp.push_back(bp);
+            } else {
+                b = it->second;
+            }
+            tmp[b].members.push_back(i);
+        }
+        // order buckets by executed cost, descending; stable sort keeps first appearance on ties
+        for (auto& bp : tmp) bp.exec_cost = (int64_t)bp.members.size() * dense_cost(bp.m_pad, bp.n_pad);
+        std::vector<int32_t> idx(tmp.size());
+        for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int32_t)i;
+        std::stable_sort(idx.begin(), idx.end(),
+                         [&](int32_t x, int32_t y) { return tmp[x].exec_cost > tmp[y].exec_cost; });
+        p->buckets.reserve(tmp.size());
+        for (int32_t b : idx) p->buckets.push_back(std::move(tmp[b]));
+
+        // plan order, slots, norm partial offsets
+        p->order.reserve(count);
+        int64_t partials = 0;
+        for (int32_t b = 0; b < (int32_t)p->buckets.size(); ++b) {
+            BucketPlan& bp = p->buckets[b];
+            bp.plan_base = (int32_t)p->order.size();
+            for (int32_t s = 0; s < (int32_t)bp.members.size(); ++s) {
+                MatPlan& mp = p->mats[bp.members[s]];
+                mp.bucket = b;
+                mp.slot = s;
+                mp.plan_index = (int32_t)p->order.size();
+                p->order.push_back(bp.members[s]);
+            }
+        }
+        for (int32_t pi = 0; pi < count; ++pi) {
+            MatPlan& mp = p->mats[p->order[pi]];
+            mp.partial_off = partials;
+            partials += mp.prep_tiles;
+        }
+        p->total_prep_tiles = partials;
+
+        // workspace layout
+        std::size_t off = 0;
+        p->off_records = off;
+        off = align_up(off + sizeof(DevMatRec) * (std::size_t)count);
+        p->off_scale = off;
+        off = align_up(off + sizeof(float) * (std::size_t)count);
+        p->off_partials = off;
+        off = align_up(off + sizeof(float) * (std::size_t)partials);
+        for (BucketPlan& bp : p->buckets) {
+            const std::size_t cnt = bp.members.size();
+            const std::size_t xsz = (std::size_t)bp.m_pad * bp.n_pad * bp.esize;
+            const std::size_t asz = (std::size_t)bp.m_pad * bp.m_pad * bp.esize;
+            bp.off_x = off;   off = align_up(off + cnt * xsz);
+            bp.off_xt0 = off; off = align_up(off + cnt * xsz);
+            bp.off_xt1 = off; off = align_up(off + cnt * xsz);
+            bp.off_a = off;   off = align_up(off + cnt * asz);
+            bp.off_b = off;   off = align_up(off + cnt * asz);
+        }
+        p->workspace_bytes = count == 0 ? 0 : off;
+    } catch (const std::bad_alloc&) {
+        delete p;
+        return DMUON_ERR_ALLOC;
+    }
+    *out = p;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_workspace_bytes(const dmuon_plan* plan, size_t* bytes) {
+    if (plan == nullptr || bytes == nullptr) return DMUON_ERR_INVALID_ARG;
+    *bytes = plan->workspace_bytes;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_info(const dmuon_plan* plan, int32_t* count, int32_t* num_buckets) {
+    if (plan == nullptr) return DMUON_ERR_INVALID_ARG;
+    if (count) *count = (int32_t)plan->mats.size();
+    if (num_buckets) *num_buckets = (int32_t)plan->buckets.size();
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_query(const dmuon_plan* plan, int32_t idx, int32_t* bucket,
+                                        int32_t* slot, int32_t* transposed, int64_t* padded_m,
+                                        int64_t* padded_n, int64_t* ns_cost) {
+    if (plan == nullptr || idx < 0 || idx >= (int32_t)plan->mats.size()) return DMUON_ERR_INVALID_ARG;
+    const MatPlan& mp = plan->mats[idx];
+    if (bucket) *bucket = mp.bucket;
+    if (slot) *slot = mp.slot;
+    if (transposed) *transposed = mp.transposed;
+    if (padded_m) *padded_m = mp.m_pad;
+    if (padded_n) *padded_n = mp.n_pad;
+    if (ns_cost) *ns_cost = mp.cost;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket, int32_t* path,
+                                         int64_t* padded_m, int64_t* padded_n, int32_t* count,
+                                         int32_t* tile) {
+    if (plan == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size())
+        return DMUON_ERR_INVALID_ARG;
+    const BucketPlan& bp = plan->buckets[bucket];
+    if (path) *path = bp.path;
+    if (padded_m) *padded_m = bp.m_pad;
+    if (padded_n) *padded_n = bp.n_pad;
+    if (count) *count = (int32_t)bp.members.size();
+    if (tile) *tile = bp.tile;
+    return DMUON_OK;
+}
+
+extern "C" void muon_plan_destroy(dmuon_plan* plan) { delete plan; }
+
+extern "C" const char* dmuon_status_string(dmuon_status status) {
+    switch (status) {
+        case DMUON_OK: return "ok";
+        case DMUON_ERR_INVALID_ARG: return "invalid argument";
+        case DMUON_ERR_UNSUPPORTED: return "unsupported";
+        case DMUON_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case DMUON_ERR_HIP: return "HIP runtime error";
+        case DMUON_ERR_ALLOC: return "host allocation failed";
+    }
+    return "unknown status";
+}
+
+extern "C" const char* dmuon_version(void) { return "0.1.0"; }

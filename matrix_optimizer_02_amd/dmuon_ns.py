@@ -1,0 +1,356 @@
+"""Python binding of libdmuon_ns (ctypes): the C ABI's entry points under the
+same names, plus argument marshalling.
+
+Every step of the Muon path runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers and the current torch stream into a
+hipStream_t.  PyTorch provides device memory and streams, nothing else.  If the
+library is not built, importing this module raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loads the HIP runtime the library binds to
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmuon_ns.so")
+
+DMUON_OK = 0
+DMUON_ERR_INVALID_ARG = -1
+DMUON_ERR_UNSUPPORTED = -2
+DMUON_ERR_WORKSPACE = -3
+DMUON_ERR_HIP = -4
+DMUON_ERR_ALLOC = -5
+
+DMUON_F32 = 0
+DMUON_BF16 = 1
+
+_DTYPE_CODE = {torch.float32: DMUON_F32, torch.bfloat16: DMUON_BF16,
+               "f32": DMUON_F32, "bf16": DMUON_BF16}
+_CODE_DTYPE = {DMUON_F32: torch.float32, DMUON_BF16: torch.bfloat16}
+
+
+class DMuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class MatrixDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("grad_dtype", ctypes.c_int32), ("param_dtype", ctypes.c_int32)]
+
+
+class HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("eps", ctypes.c_float),
+                ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
+                ("ns_steps", ctypes.c_int32), ("nesterov", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run `python -m matrix_optimizer_02_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    c_int32_p = ctypes.POINTER(ctypes.c_int32)
+    c_int64_p = ctypes.POINTER(ctypes.c_int64)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "muon_plan": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, vpp]),
+        "muon_plan_workspace_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "muon_plan_info": (ctypes.c_int, [ctypes.c_void_p, c_int32_p, c_int32_p]),
+        "muon_plan_query": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p,
+                                           c_int32_p, c_int64_p, c_int64_p, c_int64_p]),
+        "muon_plan_bucket": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int64_p,
+                                            c_int64_p, c_int32_p, c_int32_p]),
+        "muon_plan_destroy": (None, [ctypes.c_void_p]),
+        "muon_step_batched": (ctypes.c_int, [ctypes.c_void_p, vpp, vpp, vpp, ctypes.POINTER(HParams),
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "ns_orthogonalize_batched": (ctypes.c_int, [ctypes.c_void_p, vpp, vpp, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                    ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                                    ctypes.c_void_p]),
+        "muon_step_batched_profiled": (ctypes.c_int, [ctypes.c_void_p, vpp, vpp, vpp, ctypes.POINTER(HParams),
+                                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                      vpp, ctypes.c_int32]),
+        "muon_step_event_count": (ctypes.c_int32, [ctypes.c_int32]),
+        "dmuon_events_create": (ctypes.c_int, [ctypes.c_int32, vpp]),
+        "dmuon_events_elapsed_ms": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.POINTER(ctypes.c_float)]),
+        "dmuon_events_destroy": (ctypes.c_int, [ctypes.c_int32, vpp]),
+        "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "dmuon_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _lib.dmuon_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.dmuon_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != DMUON_OK:
+        raise DMuonError(status, where)
+
+
+@dataclasses.dataclass(frozen=True)
+class PlanEntry:
+    bucket: int
+    slot: int
+    transposed: bool
+    padded_m: int
+    padded_n: int
+    ns_cost: int
+
+
+@dataclasses.dataclass(frozen=True)
+class BucketEntry:
+    path: int
+    padded_m: int
+    padded_n: int
+    count: int
+    tile: int
+
+
+class Plan:
+    """Owner of a dmuon_plan (host memory only)."""
+
+    def __init__(self, descs: Sequence[tuple]):
+        """descs: (rows, cols, grad_dtype, param_dtype); dtypes as torch dtypes,
+        "bf16"/"f32" or the DMUON_* codes."""
+        self.descs = [(int(r), int(c), _code(g), _code(p)) for (r, c, g, p) in descs]
+        arr = (MatrixDesc * max(1, len(self.descs)))()
+        for i, (r, c, g, p) in enumerate(self.descs):
+            arr[i] = MatrixDesc(r, c, g, p)
+        handle = ctypes.c_void_p()
+        self._destroy = _lib.muon_plan_destroy
+        _check(_lib.muon_plan(arr, len(self.descs), ctypes.byref(handle)), "muon_plan")
+        self._h = handle
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def __len__(self):
+        return len(self.descs)
+
+    def workspace_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        _check(_lib.muon_plan_workspace_bytes(self._h, ctypes.byref(n)), "muon_plan_workspace_bytes")
+        return n.value
+
+    def info(self):
+        c, b = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.muon_plan_info(self._h, ctypes.byref(c), ctypes.byref(b)), "muon_plan_info")
+        return c.value, b.value
+
+    def query(self, idx: int) -> PlanEntry:
+        b, s, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        pm, pn, cost = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(_lib.muon_plan_query(self._h, int(idx), ctypes.byref(b), ctypes.byref(s), ctypes.byref(t),
+                                    ctypes.byref(pm), ctypes.byref(pn), ctypes.byref(cost)),
+               "muon_plan_query")
+        return PlanEntry(b.value, s.value, bool(t.value), pm.value, pn.value, cost.value)
+
+    def bucket(self, b: int) -> BucketEntry:
+        path, cnt, tile = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        pm, pn = ctypes.c_int64(), ctypes.c_int64()
+        _check(_lib.muon_plan_bucket(self._h, int(b), ctypes.byref(path), ctypes.byref(pm), ctypes.byref(pn),
+                                     ctypes.byref(cnt), ctypes.byref(tile)), "muon_plan_bucket")
+        return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
+
+
+def _code(d) -> int:
+    if isinstance(d, int):
+        return d
+    return _DTYPE_CODE[d]
+
+
+def muon_plan(descs: Sequence[tuple]) -> Plan:
+    return Plan(descs)
+
+
+def plan_for(tensors_or_shapes: Sequence, param_dtypes: Optional[Sequence] = None) -> Plan:
+    """Plan from gradient tensors (shape and dtype) and parameter dtypes."""
+    descs = []
+    for i, g in enumerate(tensors_or_shapes):
+        pd = g.dtype if param_dtypes is None else param_dtypes[i]
+        descs.append((g.shape[0], g.shape[1], g.dtype, pd))
+    return Plan(descs)
+
+
+def workspace_for(plan: Plan, device=None) -> torch.Tensor:
+    """A device byte buffer of the plan's workspace size (torch's allocator
+    returns 256-byte aligned blocks)."""
+    n = max(plan.workspace_bytes(), 1)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def _ptr_array(ts: Sequence[torch.Tensor]):
+    arr = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _check_tensors(plan: Plan, ts: Sequence[torch.Tensor], which: str, dtype_of):
+    if len(ts) != len(plan.descs):
+        raise ValueError(f"{which}: expected {len(plan.descs)} tensors, got {len(ts)}")
+    for i, (t, d) in enumerate(zip(ts, plan.descs)):
+        if not t.is_cuda:
+            raise ValueError(f"{which}[{i}] must be a device tensor")
+        if tuple(t.shape) != (d[0], d[1]) or not t.is_contiguous():
+            raise ValueError(f"{which}[{i}]: expected contiguous {d[0]}x{d[1]}, got {tuple(t.shape)}")
+        want = dtype_of(d)
+        if t.dtype != want:
+            raise ValueError(f"{which}[{i}]: expected {want}, got {t.dtype}")
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def muon_step_batched(plan: Plan, grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
+                      params: Sequence[torch.Tensor], *, lr: float = 0.02, beta: float = 0.95,
+                      weight_decay: float = 0.0, eps: float = 1e-7,
+                      a: float = 3.4445, b: float = -4.7750, c: float = 2.0315, ns_steps: int = 5,
+                      nesterov: bool = True, workspace: torch.Tensor = None, stream=None) -> None:
+    """Enqueue one fused Muon step on ``stream`` (default: torch's current
+    stream).  momenta and params are updated in place."""
+    _check_tensors(plan, grads, "grads", lambda d: _CODE_DTYPE[d[2]])
+    _check_tensors(plan, momenta, "momenta", lambda d: torch.float32)
+    _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
+    if workspace is None:
+        raise ValueError("workspace is required (see workspace_for)")
+    hp = HParams(lr, beta, weight_decay, eps, a, b, c, int(ns_steps), 1 if nesterov else 0)
+    g, m, p = _ptr_array(grads), _ptr_array(momenta), _ptr_array(params)
+    st = _lib.muon_step_batched(plan.handle, ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)),
+                                ctypes.cast(m, ctypes.POINTER(ctypes.c_void_p)),
+                                ctypes.cast(p, ctypes.POINTER(ctypes.c_void_p)), ctypes.byref(hp),
+                                ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(st, "muon_step_batched")
+
+
+def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor],
+                             *, ns_steps: int = 5, a: float = 3.4445, b: float = -4.7750,
+                             c: float = 2.0315, eps: float = 1e-7, workspace: torch.Tensor = None,
+                             stream=None) -> None:
+    """Enqueue outputs[i] = NS(inputs[i]) on ``stream``."""
+    _check_tensors(plan, inputs, "inputs", lambda d: _CODE_DTYPE[d[2]])
+    _check_tensors(plan, outputs, "outputs", lambda d: _CODE_DTYPE[d[3]])
+    if workspace is None:
+        raise ValueError("workspace is required (see workspace_for)")
+    i_arr, o_arr = _ptr_array(inputs), _ptr_array(outputs)
+    st = _lib.ns_orthogonalize_batched(plan.handle, ctypes.cast(i_arr, ctypes.POINTER(ctypes.c_void_p)),
+                                       ctypes.cast(o_arr, ctypes.POINTER(ctypes.c_void_p)),
+                                       int(ns_steps), a, b, c, eps, ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream))
+    _check(st, "ns_orthogonalize_batched")
+
+
+class PhaseEvents:
+    """HIP events for muon_step_batched_profiled: one set per step to time."""
+
+    PHASES_PER_ITER = ("gram", "square", "bx")
+
+    def __init__(self, ns_steps: int):
+        self.ns_steps = int(ns_steps)
+        self.n = _lib.muon_step_event_count(self.ns_steps)
+        self.arr = (ctypes.c_void_p * self.n)()
+        self._destroy = _lib.dmuon_events_destroy
+        _check(_lib.dmuon_events_create(self.n, ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p))),
+               "dmuon_events_create")
+
+    def names(self) -> List[str]:
+        out = ["prep"]
+        for it in range(self.ns_steps):
+            out += [f"{p}{it}" for p in self.PHASES_PER_ITER]
+        return out + ["apply"]
+
+    def elapsed_ms(self) -> List[float]:
+        """Per-phase milliseconds (waits for the last event)."""
+        res = []
+        for k in range(self.n - 1):
+            ms = ctypes.c_float()
+            _check(_lib.dmuon_events_elapsed_ms(self.arr[k], self.arr[k + 1], ctypes.byref(ms)),
+                   "dmuon_events_elapsed_ms")
+            res.append(ms.value)
+        return res
+
+    def close(self):
+        if getattr(self, "arr", None) is not None:
+            self._destroy(self.n, ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p)))
+            self.arr = None
+
+    def __del__(self):
+        self.close()
+
+
+def muon_step_batched_profiled(plan: Plan, grads, momenta, params, events: PhaseEvents, *,
+                               lr: float = 0.02, beta: float = 0.95, weight_decay: float = 0.0,
+                               eps: float = 1e-7, a: float = 3.4445, b: float = -4.7750,
+                               c: float = 2.0315, nesterov: bool = True,
+                               workspace: torch.Tensor = None, stream=None) -> None:
+    """muon_step_batched with a HIP event recorded at every phase boundary."""
+    _check_tensors(plan, grads, "grads", lambda d: _CODE_DTYPE[d[2]])
+    _check_tensors(plan, momenta, "momenta", lambda d: torch.float32)
+    _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
+    if workspace is None:
+        raise ValueError("workspace is required (see workspace_for)")
+    hp = HParams(lr, beta, weight_decay, eps, a, b, c, events.ns_steps, 1 if nesterov else 0)
+    g, m, p = _ptr_array(grads), _ptr_array(momenta), _ptr_array(params)
+    vp = ctypes.POINTER(ctypes.c_void_p)
+    st = _lib.muon_step_batched_profiled(plan.handle, ctypes.cast(g, vp), ctypes.cast(m, vp), ctypes.cast(p, vp),
+                                         ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                                         workspace.numel() * workspace.element_size(), _stream_handle(stream),
+                                         ctypes.cast(events.arr, vp), events.n)
+    _check(st, "muon_step_batched_profiled")
+
+
+class MuonBatch:
+    """Convenience owner of a plan and its workspace for a fixed matrix set."""
+
+    def __init__(self, grads: Sequence[torch.Tensor], params: Sequence[torch.Tensor]):
+        self.plan = plan_for(grads, [p.dtype for p in params])
+        self.workspace = workspace_for(self.plan, grads[0].device if len(grads) else None)
+
+    def step(self, grads, momenta, params, **hp):
+        muon_step_batched(self.plan, grads, momenta, params, workspace=self.workspace, **hp)
+
+    def orthogonalize(self, inputs, outputs, **kw):
+        ns_orthogonalize_batched(self.plan, inputs, outputs, workspace=self.workspace, **kw)
+
+
+__all__ = ["Plan", "PlanEntry", "BucketEntry", "MuonBatch", "DMuonError", "PhaseEvents", "muon_plan",
+           "plan_for", "workspace_for", "muon_step_batched", "muon_step_batched_profiled",
+           "ns_orthogonalize_batched", "status_string",
+           "version", "library_path", "DMUON_F32", "DMUON_BF16"]
