@@ -101,6 +101,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3.1-8b_owner_1of8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (3 times): the reference "
+                         "dispatch for scaling HBM traffic counters")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -119,6 +122,15 @@ def main(argv=None):
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
+        return 0
     w = get_workload(args.workload)
     G, M, W = make_inputs(w, dev, seed=args.seed)
     paths = {s.grad_dtype for s in w.matrices}

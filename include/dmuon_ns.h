@@ -109,8 +109,8 @@ typedef struct dmuon_plan dmuon_plan; /* opaque, host memory only, immutable onc
 DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
 
 /* Bytes of device workspace a step or orthogonalisation with this plan needs
- * (0 for an empty plan).  The workspace holds the per-bucket X, X^T (two
- * copies), A and B operands, per-matrix norms and a small descriptor table;
+ * (0 for an empty plan).  The workspace holds the per-bucket X (two copies),
+ * A and B operands, per-matrix norms and a small descriptor table;
  * its contents need no initialisation and are garbage after a call. */
 DMUON_API dmuon_status muon_plan_workspace_bytes(const dmuon_plan* plan, size_t* bytes);
 

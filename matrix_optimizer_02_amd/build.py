@@ -56,28 +56,33 @@ def exported_symbols():
     return re.findall(r"^DMUON_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libdmuon_ns.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = None, build_dir: str = None) -> str:
+    """Compile every source and link libdmuon_ns.so; returns the library path.
+    ``extra_flags`` (e.g. -D tuning macros) go to every hipcc compile; ``out``
+    and ``build_dir`` redirect the library and the object files."""
+    lib = out or LIB
+    bdir = build_dir or BUILD
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cc = hipcc()
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        _run([cc, *HIP_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        obj = os.path.join(bdir, src + ".o")
+        _run([cc, *HIP_FLAGS, *extra_flags, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
         objs.append(obj)
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", f"-I{INCLUDE}", "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    version_script = os.path.join(BUILD, "exports.map")
+    version_script = os.path.join(bdir, "exports.map")
     with open(version_script, "w") as f:
         f.write("{ global: " + " ".join(s + ";" for s in exported_symbols()) + " local: *; };\n")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
           f"-Wl,--version-script={version_script}", "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

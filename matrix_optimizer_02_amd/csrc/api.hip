@@ -1,6 +1,6 @@
 // C-ABI entry points of libdmuon_ns that enqueue device work: argument checks,
 // the per-call matrix table, and the launch sequence of one step
-//   records -> prep (momentum, U, X, X^T, norm partials) -> norms
+//   records -> prep (momentum, U, X, norm partials) -> norms
 //   -> ns_steps x (Gram, square, BX), each one grouped launch per tile class
 //   -> apply (update or output).
 // No device memory is allocated and nothing is synchronised: everything is
@@ -83,9 +83,8 @@ hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const
             s.first_block = ga.total_blocks;
             s.m_pad = bp.m_pad;
             s.n_pad = bp.n_pad;
-            s.x_off = (int64_t)bp.off_x;
-            s.xt_src_off = (int64_t)(iter % 2 == 0 ? bp.off_xt0 : bp.off_xt1);
-            s.xt_dst_off = (int64_t)(iter % 2 == 0 ? bp.off_xt1 : bp.off_xt0);
+            s.x_src_off = (int64_t)(iter % 2 == 0 ? bp.off_x0 : bp.off_x1);
+            s.x_dst_off = (int64_t)(iter % 2 == 0 ? bp.off_x1 : bp.off_x0);
             s.a_off = (int64_t)bp.off_a;
             s.b_off = (int64_t)bp.off_b;
             s.x_stride = bp.m_pad * bp.n_pad * bp.esize;
@@ -129,9 +128,8 @@ dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hip
         r.src = sp.src[in];
         r.mom = sp.mom ? sp.mom[in] : nullptr;
         r.dst = sp.dst[in];
-        r.x_off = (int64_t)bp.off_x + mp.slot * xsz;
-        r.xt_off0 = (int64_t)bp.off_xt0 + mp.slot * xsz;
-        r.xt_off1 = (int64_t)bp.off_xt1 + mp.slot * xsz;
+        r.x_off0 = (int64_t)bp.off_x0 + mp.slot * xsz;
+        r.x_off1 = (int64_t)bp.off_x1 + mp.slot * xsz;
         r.partial_off = mp.partial_off;
         r.prep_begin = prep_blocks;
         prep_blocks += mp.prep_tiles;

@@ -43,8 +43,9 @@ struct BucketPlan {
     int64_t exec_cost;     // count * (4 m_pad^2 n_pad + 2 m_pad^3)
     int32_t esize;         // bytes per element of X / A / B
     // byte offsets of the bucket's arrays in the workspace; slot s of array Y
-    // starts at off_Y + s * (its per-matrix size)
-    std::size_t off_x, off_xt0, off_xt1, off_a, off_b;
+    // starts at off_Y + s * (its per-matrix size).  X (m_pad x n_pad) is kept in
+    // two copies that the iterations ping-pong between.
+    std::size_t off_x0, off_x1, off_a, off_b;
 };
 
 }  // namespace dmuon
@@ -66,9 +67,8 @@ struct DevMatRec {
     const void* src;       // gradient (step) or input (orthogonalisation)
     float* mom;            // momentum, nullptr for orthogonalisation
     void* dst;             // parameter (step) or output (orthogonalisation)
-    int64_t x_off;         // byte offset of this matrix's X in the workspace
-    int64_t xt_off0;       // ... of X^T copy 0
-    int64_t xt_off1;       // ... of X^T copy 1
+    int64_t x_off0;        // byte offset of this matrix's X copy 0 in the workspace
+    int64_t x_off1;        // ... of X copy 1
     int64_t partial_off;   // first norm partial
     int64_t prep_begin;    // first prep block of this matrix (prefix sum)
     int64_t apply_begin;   // first apply block of this matrix (prefix sum)

@@ -1,11 +1,13 @@
 // Bandwidth-bound passes of the owner-side Muon step (gfx950):
 //   prep   -- momentum accumulation, the Nesterov look-ahead U, U cast to the
-//             NS operand dtype and written in both orientations (X: m x n and
-//             X^T: n x m, zero padded), and per-tile partial sums of U^2;
+//             NS operand dtype and written as X (m x n, short side first:
+//             transposed for tall matrices, zero padded), and per-tile partial
+//             sums of U^2;
 //   norms  -- per matrix, the fixed-order sum of those partials:
 //             scale = 1 / (||U||_F + eps);
 //   apply  -- the parameter update W' = W (1 - lr wd) - lr s O, or the output
-//             O, read from the final X / X^T in the stored orientation.
+//             O, read from the final X back in the stored orientation
+//             (transposed through LDS for tall matrices).
 // The normalisation itself is folded into the first Newton-Schulz
 // iteration's epilogues (A0 = scale^2 U U^T, X1 = scale (a U + B0 U)), so U
 // is read from HBM once.
@@ -29,7 +31,9 @@ __global__ void write_records_kernel(RecChunk c) {
 
 // ---- prep ---------------------------------------------------------------------
 // One block per 64 x 64 tile of the padded stored-orientation matrix.  Thread
-// t covers columns 4 (t % 16) .. +3 of rows t / 16 + 16 p, p = 0..3.
+// t covers columns 4 (t % 16) .. +3 of rows t / 16 + 16 p, p = 0..3.  X is
+// m_pad x n_pad: for a wide or square matrix it is U itself, for a tall one
+// U^T, written from the LDS copy of the tile so both sides stay coalesced.
 template <typename T, bool VEC>
 __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r, int64_t local,
                                           float (*tile)[kPrepTile + 1], float* red) {
@@ -39,8 +43,7 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
     const int t = threadIdx.x, cg = t & 15, rr = t >> 4;
     const T* G = static_cast<const T*>(r.src);
     float* M = r.mom;
-    T* D = reinterpret_cast<T*>(a.ws + (r.transposed ? r.xt_off0 : r.x_off));  // stored orientation
-    T* E = reinterpret_cast<T*>(a.ws + (r.transposed ? r.x_off : r.xt_off0));  // the other one
+    T* X = reinterpret_cast<T*>(a.ws + r.x_off0);
     const float beta = a.beta;
     float ss = 0.f;
     #pragma unroll
@@ -91,17 +94,22 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
             }
         }
         ss += u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + u[3] * u[3];
-        store4(D + rho * r.c_pad + kap, make_float4(u[0], u[1], u[2], u[3]));
-        #pragma unroll
-        for (int q = 0; q < 4; ++q) tile[row][4 * cg + q] = u[q];
+        if (!r.transposed) {
+            store4(X + rho * r.c_pad + kap, make_float4(u[0], u[1], u[2], u[3]));
+        } else {
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) tile[row][4 * cg + q] = u[q];
+        }
     }
-    __syncthreads();
-    #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int row_e = rr + 16 * p;  // column offset in the stored orientation
-        const float4 v = make_float4(tile[4 * cg + 0][row_e], tile[4 * cg + 1][row_e],
-                                     tile[4 * cg + 2][row_e], tile[4 * cg + 3][row_e]);
-        store4(E + (kap0 + row_e) * r.r_pad + rho0 + 4 * cg, v);
+    if (r.transposed) {
+        __syncthreads();
+        #pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row_e = rr + 16 * p;  // column offset in the stored orientation
+            const float4 v = make_float4(tile[4 * cg + 0][row_e], tile[4 * cg + 1][row_e],
+                                         tile[4 * cg + 2][row_e], tile[4 * cg + 3][row_e]);
+            store4(X + (kap0 + row_e) * r.r_pad + rho0 + 4 * cg, v);
+        }
     }
     const float total = block_sum<kThreads>(ss, red);
     if (t == 0) a.partials[r.partial_off + local] = total;
@@ -140,48 +148,68 @@ __global__ __launch_bounds__(kThreads) void finalize_norms_kernel(const DevMatRe
 
 // ---- apply ----------------------------------------------------------------------
 // One block per 64 x 64 tile of the real (unpadded) matrix, stored orientation.
+// O is the final X (m_pad x n_pad) for a wide or square matrix and its
+// transpose for a tall one; the transposed tile goes through LDS.
 template <typename FT, typename DT, bool VEC>
 __device__ __forceinline__ void apply_tile(const ApplyArgs& a, const DevMatRec& r, int plan_idx,
-                                           int64_t local) {
+                                           int64_t local, float (*tile)[kPrepTile + 1]) {
     const int64_t tiles_c = (r.cols + kPrepTile - 1) / kPrepTile;
     const int64_t rho0 = (local / tiles_c) * kPrepTile;
     const int64_t kap0 = (local % tiles_c) * kPrepTile;
     const int t = threadIdx.x, cg = t & 15, rr = t >> 4;
-    const int64_t f_off = r.transposed ? (a.final_copy ? r.xt_off1 : r.xt_off0) : r.x_off;
-    const FT* F = reinterpret_cast<const FT*>(a.ws + f_off);
+    const FT* F = reinterpret_cast<const FT*>(a.ws + (a.final_copy ? r.x_off1 : r.x_off0));
     DT* W = static_cast<DT*>(r.dst);
     const float sigma = a.use_scale ? a.scale[plan_idx] : 1.0f;
     const float coef = -a.lr * r.upd_scale * sigma;
     const float keep = 1.0f - a.lr * a.weight_decay;
+    if (r.transposed) {
+        // X rows kap0 .. kap0 + 63, columns rho0 .. rho0 + 63 (inside the padding)
+        #pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = rr + 16 * p;
+            const float4 v = load4(F + (kap0 + row) * r.r_pad + rho0 + 4 * cg);
+            tile[4 * cg + 0][row] = v.x;
+            tile[4 * cg + 1][row] = v.y;
+            tile[4 * cg + 2][row] = v.z;
+            tile[4 * cg + 3][row] = v.w;
+        }
+        __syncthreads();
+    }
     #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int64_t rho = rho0 + rr + 16 * p;
+        const int row = rr + 16 * p;
+        const int64_t rho = rho0 + row;
         const int64_t kap = kap0 + 4 * cg;
         if (rho >= r.rows) continue;
         const int64_t e = rho * r.cols + kap;
-        const FT* f = F + rho * r.c_pad + kap;
+        float o[4];
+        if (r.transposed) {
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = tile[row][4 * cg + q];
+        } else {
+            const float4 v = load4(F + rho * r.c_pad + kap);
+            o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+        }
         if (VEC) {
             if (kap >= r.cols) continue;
-            const float4 o = load4(f);
             float4 w;
             if (a.update) {
                 w = load4(W + e);
-                w.x = fmaf(coef, o.x, keep * w.x);
-                w.y = fmaf(coef, o.y, keep * w.y);
-                w.z = fmaf(coef, o.z, keep * w.z);
-                w.w = fmaf(coef, o.w, keep * w.w);
+                w.x = fmaf(coef, o[0], keep * w.x);
+                w.y = fmaf(coef, o[1], keep * w.y);
+                w.z = fmaf(coef, o[2], keep * w.z);
+                w.w = fmaf(coef, o[3], keep * w.w);
             } else {
-                w = make_float4(sigma * o.x, sigma * o.y, sigma * o.z, sigma * o.w);
+                w = make_float4(sigma * o[0], sigma * o[1], sigma * o[2], sigma * o[3]);
             }
             store4(W + e, w);
         } else {
             #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (kap + q >= r.cols) break;
-                const float o = Elem<FT>::load(f + q);
                 float w;
-                if (a.update) w = fmaf(coef, o, keep * Elem<DT>::load(W + e + q));
-                else w = sigma * o;
+                if (a.update) w = fmaf(coef, o[q], keep * Elem<DT>::load(W + e + q));
+                else w = sigma * o[q];
                 Elem<DT>::store(W + e + q, w);
             }
         }
@@ -189,6 +217,7 @@ __device__ __forceinline__ void apply_tile(const ApplyArgs& a, const DevMatRec& 
 }
 
 __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs a) {
+    __shared__ float tile[kPrepTile][kPrepTile + 1];
     const int64_t bid = blockIdx.x;
     const int i = upper_index(a.count, bid, [&](int k) { return a.recs[k].apply_begin; });
     const DevMatRec r = a.recs[i];
@@ -197,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs a) {
     const bool fb = r.path == kPathBF16, db = r.dst_dtype == DMUON_BF16;
 #define DMUON_APPLY(FT, DT)                                  \
     do {                                                     \
-        if (vec) apply_tile<FT, DT, true>(a, r, i, local);   \
-        else apply_tile<FT, DT, false>(a, r, i, local);      \
+        if (vec) apply_tile<FT, DT, true>(a, r, i, local, tile);   \
+        else apply_tile<FT, DT, false>(a, r, i, local, tile);      \
     } while (0)
     if (fb && db) DMUON_APPLY(uint16_t, uint16_t);
     else if (fb) DMUON_APPLY(uint16_t, float);

@@ -1,9 +1,10 @@
 // The three Newton-Schulz products in fp32 (the path taken for fp32
-// gradients), same grouped launches, tile decode and epilogues as the bf16
-// MFMA kernels: Gram A = s X X^T and square B = b A + c A A^T on upper-triangle
-// tiles with mirrored stores, X'^T = s (a X^T + X^T B^T) stored in both
-// orientations.  Products are computed with fp32 FMA on 64 x 64 tiles,
-// 256 threads, 4 x 4 outputs per thread, K staged through LDS 16 at a time.
+// gradients), same grouped launches and epilogues as the bf16 MFMA kernels:
+// Gram A = s X X^T and square B = b A + c A A^T on upper-triangle tiles with
+// mirrored stores, and X' = s (a X + B X) into the other X copy (computed as
+// X'^T tiles: rows of the long side, columns of the short side).  Products are
+// computed with fp32 FMA on 64 x 64 tiles, 256 threads, 4 x 4 outputs per
+// thread, K staged through LDS 16 at a time.
 //
 // Page basis: as for the bf16 kernels -- X X^T on the full matrix, one
 // triangle of the symmetric products (DMuon explainer on gist.science, second
@@ -46,29 +47,35 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
     const float *P, *Q;
     int64_t ldk, K;
     if (PHASE == kBX) {
-        I = t / sg.tm;
+        I = t / sg.tm;  // long-side tile
         J = t - I * sg.tm;
-        P = reinterpret_cast<const float*>(args.ws + sg.xt_src_off + slot * sg.x_stride);
+        P = reinterpret_cast<const float*>(args.ws + sg.x_src_off + slot * sg.x_stride);  // X: m x n
         Q = reinterpret_cast<const float*>(args.ws + sg.b_off + slot * sg.a_stride);
         ldk = sg.m_pad;
         K = sg.m_pad;
     } else {
         tri_decode_f(t, sg.tm, I, J);
-        const int64_t off = PHASE == kGram ? sg.x_off + slot * sg.x_stride : sg.a_off + slot * sg.a_stride;
+        const int64_t off = PHASE == kGram ? sg.x_src_off + slot * sg.x_stride : sg.a_off + slot * sg.a_stride;
         P = Q = reinterpret_cast<const float*>(args.ws + off);
         ldk = PHASE == kGram ? sg.n_pad : sg.m_pad;
         K = ldk;
     }
-    const float* Pt = P + (int64_t)I * kT * ldk;
     const float* Qt = Q + (int64_t)J * kT * ldk;
 
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int lrow = tid >> 2, lk = (tid & 3) * 4;
     float acc[4][4] = {};
     for (int64_t k0 = 0; k0 < K; k0 += kBKf) {
-        const float4 pv = *reinterpret_cast<const float4*>(Pt + lrow * ldk + k0 + lk);
+        if (PHASE == kBX) {
+            // P[j][k] = X[k][j]: X rows k0 .. k0+15, long-side columns of tile I
+            const int kk = tid >> 4, jj = (tid & 15) * 4;
+            const float4 pv = *reinterpret_cast<const float4*>(P + (k0 + kk) * sg.n_pad + (int64_t)I * kT + jj);
+            Ps[kk][jj + 0] = pv.x; Ps[kk][jj + 1] = pv.y; Ps[kk][jj + 2] = pv.z; Ps[kk][jj + 3] = pv.w;
+        } else {
+            const float4 pv = *reinterpret_cast<const float4*>(P + ((int64_t)I * kT + lrow) * ldk + k0 + lk);
+            Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
+        }
         const float4 qv = *reinterpret_cast<const float4*>(Qt + lrow * ldk + k0 + lk);
-        Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
         Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
         __syncthreads();
         #pragma unroll
@@ -89,22 +96,20 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
     const float first_scale = args.first_iter ? args.scale[plan_idx] : 1.0f;
     const int64_t r0 = (int64_t)I * kT + ty * 4, c0 = (int64_t)J * kT + tx * 4;
     if (PHASE == kBX) {
-        const int64_t ldm = sg.m_pad, ldn = sg.n_pad;
-        const float* XTs = P;
-        float* XTd = reinterpret_cast<float*>(args.ws + sg.xt_dst_off + slot * sg.x_stride);
-        float* X = reinterpret_cast<float*>(args.ws + sg.x_off + slot * sg.x_stride);
-        float o[4][4];
+        // rows r of the tile are long-side indices, columns c short-side ones:
+        // X'[c][r] = s (a X[c][r] + acc[r][c])
+        const int64_t ldn = sg.n_pad;
+        const float* Xs = P;
+        float* Xd = reinterpret_cast<float*>(args.ws + sg.x_dst_off + slot * sg.x_stride);
         #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 xs = *reinterpret_cast<const float4*>(XTs + (r0 + i) * ldm + c0);
-            const float xr[4] = {xs.x, xs.y, xs.z, xs.w};
-            #pragma unroll
-            for (int j = 0; j < 4; ++j) o[i][j] = first_scale * fmaf(args.a, xr[j], acc[i][j]);
-            *reinterpret_cast<float4*>(XTd + (r0 + i) * ldm + c0) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+        for (int j = 0; j < 4; ++j) {
+            const float4 xs = *reinterpret_cast<const float4*>(Xs + (c0 + j) * ldn + r0);
+            const float4 o = make_float4(first_scale * fmaf(args.a, xs.x, acc[0][j]),
+                                         first_scale * fmaf(args.a, xs.y, acc[1][j]),
+                                         first_scale * fmaf(args.a, xs.z, acc[2][j]),
+                                         first_scale * fmaf(args.a, xs.w, acc[3][j]));
+            *reinterpret_cast<float4*>(Xd + (c0 + j) * ldn + r0) = o;
         }
-        #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4*>(X + (c0 + j) * ldn + r0) = make_float4(o[0][j], o[1][j], o[2][j], o[3][j]);
     } else {
         const int64_t ld = sg.m_pad;
         const int64_t out_off = PHASE == kGram ? sg.a_off + slot * sg.a_stride : sg.b_off + slot * sg.a_stride;

@@ -40,7 +40,7 @@ struct ApplyArgs {
     int32_t count;
     const char* ws;
     const float* scale;
-    int32_t final_copy;    // which X^T copy holds the result (ns_steps % 2)
+    int32_t final_copy;    // which X copy holds the result (ns_steps % 2)
     int32_t use_scale;     // ns_steps == 0: multiply by 1 / (||U|| + eps)
     int32_t update;        // 1: W' = W (1 - lr wd) - lr s O ; 0: dst = O
     float lr;
@@ -63,7 +63,7 @@ struct GemmSeg {
     int32_t count;          // matrices in the bucket
     int32_t plan_base;      // plan index of slot 0
     int64_t m_pad, n_pad;
-    int64_t x_off, xt_src_off, xt_dst_off, a_off, b_off;  // bucket base byte offsets
+    int64_t x_src_off, x_dst_off, a_off, b_off;  // bucket base byte offsets (X read / written)
     int64_t x_stride, a_stride;                           // per-slot bytes
 };
 

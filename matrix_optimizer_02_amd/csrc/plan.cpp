@@ -127,9 +127,8 @@ extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count,
             const std::size_t cnt = bp.members.size();
             const std::size_t xsz = (std::size_t)bp.m_pad * bp.n_pad * bp.esize;
             const std::size_t asz = (std::size_t)bp.m_pad * bp.m_pad * bp.esize;
-            bp.off_x = off;   off = align_up(off + cnt * xsz);
-            bp.off_xt0 = off; off = align_up(off + cnt * xsz);
-            bp.off_xt1 = off; off = align_up(off + cnt * xsz);
+            bp.off_x0 = off;  off = align_up(off + cnt * xsz);
+            bp.off_x1 = off;  off = align_up(off + cnt * xsz);
             bp.off_a = off;   off = align_up(off + cnt * asz);
             bp.off_b = off;   off = align_up(off + cnt * asz);
         }

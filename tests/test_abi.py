@@ -80,7 +80,7 @@ def test_workspace_covers_operands():
     for bk in buckets:
         es = 2 if bk["path"] == "bf16" else 4
         cnt = len(bk["members"])
-        need += cnt * es * (3 * bk["m_pad"] * bk["n_pad"] + 2 * bk["m_pad"] ** 2)
+        need += cnt * es * (2 * bk["m_pad"] * bk["n_pad"] + 2 * bk["m_pad"] ** 2)
     assert d.Plan(descs).workspace_bytes() >= need
     assert d.Plan([]).workspace_bytes() == 0
 
