@@ -40,6 +40,9 @@
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
 #endif
+#ifndef DMUON_L2_PREFETCH
+#define DMUON_L2_PREFETCH 0
+#endif
 
 namespace dmuon {
 namespace {
@@ -91,7 +94,9 @@ __device__ __forceinline__ int swizzle_e(int r) { return r & (T / 8 - 1); }
 template <int T, int PHASE, int S>
 __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T, S>;
-    __shared__ __attribute__((aligned(1024))) char smem[S * C::kStageBytes];
+    // S stages, then 1 KB that L2 prefetches land in (never read)
+    __shared__ __attribute__((aligned(1024))) char smem[S * C::kStageBytes + 1024];
+    constexpr bool kPrefetch = DMUON_L2_PREFETCH && S == 2 && kBK == 64;
     static_assert(PHASE != kBX || S * C::kStageBytes >= 2 * T * T, "B X epilogue tile fits the stages");
 
     // ---- which tile of which matrix --------------------------------------------
@@ -174,6 +179,31 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         }
     };
 
+    // L2 prefetch of a slab: every 128-byte line of both operand slabs is
+    // touched by one lane (4 bytes, landing in the scratch KB), so the slab's
+    // direct loads issued one slab later hit L2.  Every wave issues the same
+    // number of them (one per operand; T = 128 touches some lines twice), which
+    // keeps the load counts the waits rely on uniform.
+    constexpr int kLinesPerOp = T * kRowBytes / 128;  // = kBK * 2 T / 128 for the B X P slab
+    constexpr int kPfPerOp = kLinesPerOp / 256 > 0 ? kLinesPerOp / 256 : 1;
+    auto prefetch = [&](int64_t k0) {
+        char* scratch = smem + S * C::kStageBytes;
+        #pragma unroll
+        for (int i = 0; i < kPfPerOp; ++i) {
+            const int id = ((wave * kPfPerOp + i) * 64 + lane) % kLinesPerOp;  // line of the slab
+            const uint16_t* gp;
+            if (PHASE == kBX) {
+                constexpr int kLinesPerRow = 2 * T / 128;
+                gp = P + (k0 + id / kLinesPerRow) * sg.n_pad + (int64_t)I * T + (id % kLinesPerRow) * 64;
+            } else {
+                gp = P + ((int64_t)I * T + id) * ldq + k0;
+            }
+            __builtin_amdgcn_global_load_lds((gptr_t)gp, (lptr_t)scratch, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((gptr_t)(Qt + (int64_t)id * ldq + k0), (lptr_t)scratch, 4, 0, 0);
+        }
+    };
+    constexpr int kPfPerSlab = kPrefetch ? 2 * kPfPerOp : 0;  // prefetch loads per wave per slab
+
     floatx16 acc[C::F][C::F];
     #pragma unroll
     for (int i = 0; i < C::F; ++i)
@@ -232,30 +262,41 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                                                                       acc[i_][j_], 0, 0, 0);      \
     } while (0)
 
-    // Wait until at most `slabs` slabs of this wave's direct loads are in flight.
-    // The compiler does not count direct-to-LDS loads in its own waits, so every
-    // wait for them is explicit.
-    static_assert(S >= 2 && S <= 5, "wait_slabs covers up to 4 slabs in flight");
+    // Wait until at most n of this wave's loads are in flight (loads complete in
+    // issue order).  The compiler does not count direct-to-LDS loads in its own
+    // waits, so every wait for them is explicit.
+    static_assert(S >= 2 && S <= 5, "waits cover up to 4 slabs in flight");
     static_assert(C::kDmaPerSlab == 16 || C::kDmaPerSlab == 8 || C::kDmaPerSlab == 4, "vmcnt encodings");
-    auto wait_slabs = [&](int slabs) {
-        const int n = slabs <= 0 ? 0 : slabs * C::kDmaPerSlab;
-        if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else if (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (n == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-        else if (n == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (n == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-        else if (n == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-        else if (n == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // any other count: drain
+    auto wait_vm = [&](int n) {
+        switch (n) {
+            case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+            case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+            case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+            case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+            case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+            case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+            case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+            case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+            case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // 0, or drain
+        }
     };
+    auto wait_slabs = [&](int slabs) { wait_vm(slabs <= 0 ? 0 : slabs * C::kDmaPerSlab); };
 
     const int KT = (int)(K / kBK);
-    // prologue: slabs 0 .. S-1 into stages 0 .. S-1; wait for slab 0
+    // prologue: slabs 0 .. S-1 into stages 0 .. S-1 (and the L2 prefetch of
+    // slab S); wait for slab 0
     #pragma unroll
     for (int st = 0; st < S; ++st)
         if (st < KT) dma((int64_t)st * kBK, st);
-    wait_slabs(min(S, KT) - 1);
+    if (kPrefetch) {
+        const bool pf = S < KT;
+        if (pf) prefetch((int64_t)S * kBK);
+        wait_vm(KT > 1 ? C::kDmaPerSlab + (pf ? kPfPerSlab : 0) : 0);
+    } else {
+        wait_slabs(min(S, KT) - 1);
+    }
     __syncthreads();
     DMUON_READ(0, smem, 0);
     constexpr int KS = kBK / 16;  // MFMA k-steps per slab (even)
@@ -290,10 +331,16 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         // landed once only the ones after it are in flight; the barrier then
         // publishes every wave's share and makes sure every wave is done
         // reading slab kt, whose stage is refilled with slab kt + S.
-        wait_slabs(min(kt + S - 1, KT - 1) - (kt + 1));
+        if (kPrefetch) {
+            // S = 2: issued after slab kt + 1's loads is only the prefetch of slab kt + 2
+            wait_vm(kt + 2 < KT ? kPfPerSlab : 0);
+        } else {
+            wait_slabs(min(kt + S - 1, KT - 1) - (kt + 1));
+        }
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         if (kt + S < KT) dma((int64_t)(kt + S) * kBK, stage);
+        if (kPrefetch && kt + S + 1 < KT) prefetch((int64_t)(kt + S + 1) * kBK);
         __builtin_amdgcn_sched_barrier(0);
         DMUON_READ(0, smem + ((kt + 1) % S) * C::kStageBytes, 0);
         DMUON_MFMA((KS - 1) & 1);
