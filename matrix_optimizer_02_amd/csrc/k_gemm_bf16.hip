@@ -18,86 +18,102 @@
 //
 // Tile: T x T outputs per 256-thread workgroup (T = 256 or 128), 4 waves in a
 // 2 x 2 grid, each wave (T/2) x (T/2) outputs as (T/64)^2 blocks of
-// v_mfma_f32_32x32x16_bf16.  K is staged through LDS in slabs by direct
-// global->LDS loads, S stages deep; 16-byte chunks are XOR-swizzled by row so
-// that the fragment reads hit distinct banks.  Each MFMA k-step is its own
+// v_mfma_f32_32x32x16_bf16.  K is staged through LDS in 64-deep slabs, two
+// stages, by direct global->LDS loads; 16-byte chunks are XOR-swizzled by row
+// so that the fragment reads hit distinct banks.  Each MFMA k-step is its own
 // scheduling region: its MFMAs interleaved with the next k-step's fragment
-// reads.  The B X epilogue stages the output tile through LDS so that both the
-// a X read and the X' write are coalesced 16-byte accesses.
+// reads and with a piece of the next slab's loads.  Every epilogue stages the
+// output tile through LDS, so that global reads and writes are whole 16-byte
+// chunks of rows.
 #include "kcommon.h"
 #include "launch.h"
 #include "tile_map.h"
 
-#ifndef DMUON_BK
-#define DMUON_BK 64
-#endif
-#ifndef DMUON_STAGES_256
-#define DMUON_STAGES_256 2
-#endif
 #ifndef DMUON_XCD_REMAP
 #define DMUON_XCD_REMAP 0
 #endif
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
 #endif
-#ifndef DMUON_L2_PREFETCH
-#define DMUON_L2_PREFETCH 0
+#ifndef DMUON_SPREAD
+#define DMUON_SPREAD 1
 #endif
 
 namespace dmuon {
 namespace {
 
-typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-constexpr int kBK = DMUON_BK;            // K slab: 32 or 64
-constexpr int kRowBytes = kBK * 2;       // one LDS row of a K-contiguous slab
-constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per such row
+constexpr int kBK = 64;                     // K slab
+constexpr int kRowBytes = kBK * 2;          // one LDS row of a K-contiguous slab
+constexpr int kChunks = kRowBytes / 16;     // 16-byte chunks per such row
 constexpr int kDmaRows = 1024 / kRowBytes;  // rows one 1 KB wave load fills
-static_assert(kBK == 32 || kBK == 64, "slab width");
+constexpr int KS = kBK / 16;                // MFMA k-steps per slab
 
-template <int T, int S>
+template <int T>
 struct TileCfg {
     static constexpr int WT = T / 2;               // wave tile
     static constexpr int F = WT / 32;              // MFMA blocks per wave per dim
     static constexpr int kDmaPerOp = T * kRowBytes / 1024 / 4;  // 1 KB loads per wave per operand per slab
-    static constexpr int kDmaPerSlab = 2 * kDmaPerOp;
     static constexpr int kOperandBytes = T * kRowBytes;
     static constexpr int kStageBytes = 2 * kOperandBytes;
     // B X: the P slab is kBK rows (k) of T long-side values
     static constexpr int kPRowBytes = 2 * T;
     static constexpr int kPChunks = kPRowBytes / 16;
     static constexpr int kPDmaRows = 1024 / kPRowBytes;
+    // epilogue tile: T rows of T bf16
+    static constexpr int kERowBytes = 2 * T;
+    static constexpr int kEChunks = T / 8;
 };
+
+// Wait until at most N of the wave's vector-memory loads are in flight (loads
+// complete in issue order).  The compiler does not count direct-to-LDS loads
+// in the waits it places before barriers, so every such wait is explicit.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One wave-wide direct load: 64 lanes x 16 bytes from global memory into the
+// 1 KB of LDS at byte offset lds (wave-uniform), lane l's bytes landing at
+// lds + 16 l.  Written as inline assembly so that the compiler, which cannot
+// tell the two slab stages apart, does not make every later LDS read wait for
+// it: the kernel orders these loads itself, with explicit waits and barriers.
+// Every direct load of the kernel goes through here, so the compiler never
+// holds a value of its own in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "m0", "memory");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(lptr_t)p;
+}
 
 // K-contiguous slab rows: logical chunk ch of row r sits at ch ^ swizzle(r), so
 // the fragment reads of 8 (or 16) consecutive rows at one logical chunk hit
 // distinct bank groups whether the LDS serves 128 or 256 bytes a clock.
-__device__ __forceinline__ int swizzle(int r) {
-    if (kBK == 32) return ((r >> 1) ^ (r >> 3)) & 3;
-    return (r & 7) ^ ((r >> 3) & 1);
-}
+__device__ __forceinline__ int swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // B X P slab (rows k, long-side columns): a transposing read takes 4 rows of
 // one 16-lane group; rows r..r+3 get chunk offsets 0, 4, 10, 14 so that the
 // 8 chunks of a group (and the 16 of two groups) fall in distinct bank groups.
 __device__ __forceinline__ int swizzle_p(int r) { return (0xEA40 >> ((r & 3) * 4)) & 15; }
 
-// B X epilogue tile (rows short side, long-side columns): one chunk swizzle
-// per row, over the row's T / 8 chunks.
+// Epilogue tile: one chunk swizzle per row, over the row's T / 8 chunks.
 template <int T>
 __device__ __forceinline__ int swizzle_e(int r) { return r & (T / 8 - 1); }
 
-template <int T, int PHASE, int S>
+template <int T, int PHASE>
 __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
-    using C = TileCfg<T, S>;
-    // S stages, then 1 KB that L2 prefetches land in (never read)
-    __shared__ __attribute__((aligned(1024))) char smem[S * C::kStageBytes + 1024];
-    constexpr bool kPrefetch = DMUON_L2_PREFETCH && S == 2 && kBK == 64;
-    static_assert(PHASE != kBX || S * C::kStageBytes >= 2 * T * T, "B X epilogue tile fits the stages");
+    using C = TileCfg<T>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
+    static_assert(2 * C::kStageBytes >= T * C::kERowBytes, "epilogue tile fits the stages");
 
     // ---- which tile of which matrix --------------------------------------------
     int s, local;
@@ -148,17 +164,18 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     const int64_t K = ldq;
     const uint16_t* Qt = Q + (int64_t)J * T * ldq;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wr = wave >> 1, wc = wave & 1;
 
-    // ---- global -> LDS (direct), S stages ---------------------------------------------
+    // ---- global -> LDS (direct) ----------------------------------------------------
     // One global_load_lds_dwordx4 of a wave fills 1 KB of LDS: lane l writes
     // bytes 16 l .. 16 l + 15 of it, so it fetches the global chunk that the
-    // swizzle places there.
-    auto dma = [&](int64_t k0, int stage) {
-        char* sbase = smem + stage * C::kStageBytes;
+    // swizzle places there.  Loads i0 .. i1-1 (of kDmaPerOp per operand) of
+    // the slab at k0 into the stage at dst.
+    auto dma_part = [&](int64_t k0, char* dst, int i0, int i1) {
         #pragma unroll
-        for (int i = 0; i < C::kDmaPerOp; ++i) {
+        for (int i = i0; i < i1; ++i) {
             const int q = wave * C::kDmaPerOp + i;  // 1 KB block of the operand slab
             const uint16_t* gp;
             if (PHASE == kBX) {
@@ -171,38 +188,18 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                 const int lc = (lane % kChunks) ^ swizzle(row);
                 gp = P + ((int64_t)I * T + row) * ldq + k0 + lc * 8;
             }
-            __builtin_amdgcn_global_load_lds((gptr_t)gp, (lptr_t)(sbase + q * 1024), 16, 0, 0);
+            dma16(gp, lds_offset(dst + q * 1024));
             const int qrow = kDmaRows * q + lane / kChunks;
             const int qlc = (lane % kChunks) ^ swizzle(qrow);
-            __builtin_amdgcn_global_load_lds((gptr_t)(Qt + (int64_t)qrow * ldq + k0 + qlc * 8),
-                                             (lptr_t)(sbase + C::kOperandBytes + q * 1024), 16, 0, 0);
+            dma16(Qt + (int64_t)qrow * ldq + k0 + qlc * 8, lds_offset(dst + C::kOperandBytes + q * 1024));
         }
     };
-
-    // L2 prefetch of a slab: every 128-byte line of both operand slabs is
-    // touched by one lane (4 bytes, landing in the scratch KB), so the slab's
-    // direct loads issued one slab later hit L2.  Every wave issues the same
-    // number of them (one per operand; T = 128 touches some lines twice), which
-    // keeps the load counts the waits rely on uniform.
-    constexpr int kLinesPerOp = T * kRowBytes / 128;  // = kBK * 2 T / 128 for the B X P slab
-    constexpr int kPfPerOp = kLinesPerOp / 256 > 0 ? kLinesPerOp / 256 : 1;
-    auto prefetch = [&](int64_t k0) {
-        char* scratch = smem + S * C::kStageBytes;
-        #pragma unroll
-        for (int i = 0; i < kPfPerOp; ++i) {
-            const int id = ((wave * kPfPerOp + i) * 64 + lane) % kLinesPerOp;  // line of the slab
-            const uint16_t* gp;
-            if (PHASE == kBX) {
-                constexpr int kLinesPerRow = 2 * T / 128;
-                gp = P + (k0 + id / kLinesPerRow) * sg.n_pad + (int64_t)I * T + (id % kLinesPerRow) * 64;
-            } else {
-                gp = P + ((int64_t)I * T + id) * ldq + k0;
-            }
-            __builtin_amdgcn_global_load_lds((gptr_t)gp, (lptr_t)scratch, 4, 0, 0);
-            __builtin_amdgcn_global_load_lds((gptr_t)(Qt + (int64_t)id * ldq + k0), (lptr_t)scratch, 4, 0, 0);
-        }
-    };
-    constexpr int kPfPerSlab = kPrefetch ? 2 * kPfPerOp : 0;  // prefetch loads per wave per slab
+    // A slab's loads go out in three pieces: the first right after the barrier
+    // that frees its stage, the other two inside the next two k-steps, so the
+    // address unit never takes a whole slab's loads at once while the matrix
+    // pipe waits behind them.
+    constexpr int kPiece1 = DMUON_SPREAD ? (3 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kPiece2 = DMUON_SPREAD ? (6 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
 
     floatx16 acc[C::F][C::F];
     #pragma unroll
@@ -225,13 +222,13 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     const int tr_sw = swizzle_p(tr_s >> 2);                           // rows are 4-aligned
     bf16x8 fa[2][C::F], fb[2][C::F];
 
-#define DMUON_READ_A(BUF, BASE, KS)                                                               \
+#define DMUON_READ_A(BUF, BASE, KS_)                                                              \
     do {                                                                                          \
         if (PHASE == kBX) {                                                                       \
             _Pragma("unroll") for (int i_ = 0; i_ < C::F; ++i_) {                                 \
                 shortx4 h_[2];                                                                    \
                 _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                \
-                    const int r_ = 16 * (KS) + 4 * t_ + tr_row;                                   \
+                    const int r_ = 16 * (KS_) + 4 * t_ + tr_row;                                  \
                     const int c_ = tr_col + 32 * i_;                                              \
                     const int o_ = r_ * C::kPRowBytes + (((c_ >> 3) ^ tr_sw) << 4) + (c_ & 7) * 2; \
                     h_[t_] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                             \
@@ -241,15 +238,15 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                 fa[BUF][i_] = __builtin_bit_cast(bf16x8, w_);                                     \
             }                                                                                     \
         } else {                                                                                  \
-            const int pc_ = ((((KS) * 2 + khalf) ^ swz) << 4);                                    \
+            const int pc_ = ((((KS_) * 2 + khalf) ^ swz) << 4);                                   \
             _Pragma("unroll") for (int i_ = 0; i_ < C::F; ++i_)                                   \
                 fa[BUF][i_] = *reinterpret_cast<const bf16x8*>((BASE) + a_row0 + i_ * 32 * kRowBytes + pc_); \
         }                                                                                         \
     } while (0)
-#define DMUON_READ(BUF, BASE, KS)                                                                 \
+#define DMUON_READ(BUF, BASE, KS_)                                                                \
     do {                                                                                          \
-        DMUON_READ_A(BUF, BASE, KS);                                                              \
-        const int pc_ = ((((KS) * 2 + khalf) ^ swz) << 4);                                        \
+        DMUON_READ_A(BUF, BASE, KS_);                                                             \
+        const int pc_ = ((((KS_) * 2 + khalf) ^ swz) << 4);                                       \
         _Pragma("unroll") for (int j_ = 0; j_ < C::F; ++j_)                                       \
             fb[BUF][j_] = *reinterpret_cast<const bf16x8*>((BASE) + C::kOperandBytes + b_row0 +     \
                                                            j_ * 32 * kRowBytes + pc_);            \
@@ -262,100 +259,81 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                                                                       acc[i_][j_], 0, 0, 0);      \
     } while (0)
 
-    // Wait until at most n of this wave's loads are in flight (loads complete in
-    // issue order).  The compiler does not count direct-to-LDS loads in its own
-    // waits, so every wait for them is explicit.
-    static_assert(S >= 2 && S <= 5, "waits cover up to 4 slabs in flight");
-    static_assert(C::kDmaPerSlab == 16 || C::kDmaPerSlab == 8 || C::kDmaPerSlab == 4, "vmcnt encodings");
-    auto wait_vm = [&](int n) {
-        switch (n) {
-            case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-            case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-            case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-            case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-            case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-            case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-            case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-            case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-            case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-            case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
-            default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // 0, or drain
-        }
-    };
-    auto wait_slabs = [&](int slabs) { wait_vm(slabs <= 0 ? 0 : slabs * C::kDmaPerSlab); };
+    constexpr int NREAD = (PHASE == kBX ? 3 : 2) * C::F;  // fragment reads per k-step
+    constexpr int NMFMA = C::F * C::F;                    // MFMAs per k-step
+    constexpr int NV1 = 2 * (kPiece2 - kPiece1);          // loads of piece 1 (k-step 0)
+    constexpr int NV2 = 2 * (C::kDmaPerOp - kPiece2);     // loads of piece 2 (k-step 1)
+    // One k-step as its own scheduling region: each of the first MFMAs is
+    // followed by one fragment read for the next k-step (and, where the region
+    // carries a piece of a slab's loads, by one of those), so the reads are in
+    // flight while the matrix pipe is busy and have landed before they are used
+    // (the MFMA leading the region only waits on reads issued a region earlier).
+#define DMUON_INTERLEAVE(NV)                                                                      \
+    do {                                                                                          \
+        _Pragma("unroll") for (int g_ = 0; g_ < NMFMA; ++g_) {                                    \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                         \
+            if (g_ < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* DS read */      \
+            if (g_ < (NV)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  /* VMEM */         \
+        }                                                                                         \
+        if (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);         \
+        if ((NV) > NMFMA) __builtin_amdgcn_sched_group_barrier(0x010, (NV) - NMFMA, 0);           \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+    } while (0)
+    // Slab KT_ (not the last) from stage CUR: pieces 1 and 2 of slab KT_ + 1
+    // go into stage OTH during the first two k-steps.  The last k-step waits
+    // for slab KT_ + 1 (nothing else is in flight then); the barrier publishes
+    // every wave's share of it and makes sure every wave is done reading CUR,
+    // which then takes the first piece of slab KT_ + 2.
+#define DMUON_SLAB(KT_, CUR, OTH)                                                                 \
+    do {                                                                                          \
+        const int64_t knext_ = (int64_t)((KT_) + 1) * kBK;                                        \
+        _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                                   \
+            if (ks == 0) dma_part(knext_, OTH, kPiece1, kPiece2);                                 \
+            if (ks == 1) dma_part(knext_, OTH, kPiece2, C::kDmaPerOp);                            \
+            DMUON_READ((ks + 1) & 1, CUR, ks + 1);                                                \
+            DMUON_MFMA(ks & 1);                                                                   \
+            if (ks == 0) DMUON_INTERLEAVE(NV1);                                                   \
+            else if (ks == 1) DMUON_INTERLEAVE(NV2);                                              \
+            else DMUON_INTERLEAVE(0);                                                             \
+        }                                                                                         \
+        wait_vm<0>();                                                                             \
+        __syncthreads();                                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+        if ((KT_) + 2 < KT) dma_part(knext_ + kBK, CUR, 0, kPiece1);                              \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+        DMUON_READ(0, OTH, 0);                                                                    \
+        DMUON_MFMA((KS - 1) & 1);                                                                 \
+        DMUON_INTERLEAVE(0);                                                                      \
+    } while (0)
+#define DMUON_LAST_SLAB(CUR)                                                                      \
+    do {                                                                                          \
+        _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                                   \
+            DMUON_READ((ks + 1) & 1, CUR, ks + 1);                                                \
+            DMUON_MFMA(ks & 1);                                                                   \
+            DMUON_INTERLEAVE(0);                                                                  \
+        }                                                                                         \
+        DMUON_MFMA((KS - 1) & 1);                                                                 \
+    } while (0)
 
     const int KT = (int)(K / kBK);
-    // prologue: slabs 0 .. S-1 into stages 0 .. S-1 (and the L2 prefetch of
-    // slab S); wait for slab 0
-    #pragma unroll
-    for (int st = 0; st < S; ++st)
-        if (st < KT) dma((int64_t)st * kBK, st);
-    if (kPrefetch) {
-        const bool pf = S < KT;
-        if (pf) prefetch((int64_t)S * kBK);
-        wait_vm(KT > 1 ? C::kDmaPerSlab + (pf ? kPfPerSlab : 0) : 0);
+    // prologue: slab 0 whole and the first piece of slab 1; wait for slab 0
+    dma_part(0, smem, 0, C::kDmaPerOp);
+    if (KT > 1) {
+        dma_part(kBK, smem + C::kStageBytes, 0, kPiece1);
+        wait_vm<2 * kPiece1>();
     } else {
-        wait_slabs(min(S, KT) - 1);
+        wait_vm<0>();
     }
     __syncthreads();
     DMUON_READ(0, smem, 0);
-    constexpr int KS = kBK / 16;  // MFMA k-steps per slab (even)
-    constexpr int NREAD = (PHASE == kBX ? 3 : 2) * C::F;  // fragment reads per k-step
-    constexpr int NMFMA = C::F * C::F;                    // MFMAs per k-step
-    // One k-step as its own scheduling region: each of the first MFMAs is
-    // followed by one fragment read for the next k-step, so the reads are in
-    // flight while the matrix pipe is busy and have landed before they are used
-    // (the MFMA leading the region only waits on reads issued a region earlier).
-#define DMUON_INTERLEAVE()                                                                        \
-    do {                                                                                          \
-        _Pragma("unroll") for (int g_ = 0; g_ < (NREAD < NMFMA ? NREAD : NMFMA); ++g_) {          \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* MFMA */                         \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* DS read */                      \
-        }                                                                                         \
-        if (NMFMA > NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);         \
-        if (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);         \
-        __builtin_amdgcn_sched_barrier(0);                                                        \
-    } while (0)
-    // all slabs but the last: the last k-step also waits for the next slab,
-    // refills the freed stage and reads the next slab's first fragments
     for (int kt = 0; kt + 1 < KT; ++kt) {
-        const int stage = kt % S;
-        const char* cur = smem + stage * C::kStageBytes;
-        #pragma unroll
-        for (int ks = 0; ks + 1 < KS; ++ks) {
-            DMUON_READ((ks + 1) & 1, cur, ks + 1);
-            DMUON_MFMA(ks & 1);
-            DMUON_INTERLEAVE();
-        }
-        // Issued so far: slabs 0 .. min(kt + S - 1, KT - 1).  Slab kt + 1 has
-        // landed once only the ones after it are in flight; the barrier then
-        // publishes every wave's share and makes sure every wave is done
-        // reading slab kt, whose stage is refilled with slab kt + S.
-        if (kPrefetch) {
-            // S = 2: issued after slab kt + 1's loads is only the prefetch of slab kt + 2
-            wait_vm(kt + 2 < KT ? kPfPerSlab : 0);
-        } else {
-            wait_slabs(min(kt + S - 1, KT - 1) - (kt + 1));
-        }
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + S < KT) dma((int64_t)(kt + S) * kBK, stage);
-        if (kPrefetch && kt + S + 1 < KT) prefetch((int64_t)(kt + S + 1) * kBK);
-        __builtin_amdgcn_sched_barrier(0);
-        DMUON_READ(0, smem + ((kt + 1) % S) * C::kStageBytes, 0);
-        DMUON_MFMA((KS - 1) & 1);
-        DMUON_INTERLEAVE();
+        char* cur = smem + (kt & 1) * C::kStageBytes;
+        char* oth = smem + ((kt + 1) & 1) * C::kStageBytes;
+        DMUON_SLAB(kt, cur, oth);
     }
-    {   // the last slab
-        const char* cur = smem + ((KT - 1) % S) * C::kStageBytes;
-        #pragma unroll
-        for (int ks = 0; ks + 1 < KS; ++ks) {
-            DMUON_READ((ks + 1) & 1, cur, ks + 1);
-            DMUON_MFMA(ks & 1);
-            DMUON_INTERLEAVE();
-        }
-        DMUON_MFMA((KS - 1) & 1);
-    }
+    DMUON_LAST_SLAB(smem + ((KT - 1) & 1) * C::kStageBytes);
+#undef DMUON_SLAB
+#undef DMUON_LAST_SLAB
 #undef DMUON_INTERLEAVE
 #undef DMUON_READ
 #undef DMUON_READ_A
@@ -363,30 +341,73 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 
     // ---- epilogue -----------------------------------------------------------------
     // acc[i][j][v] holds output row  wr*WT + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4
-    //                  and column  wc*WT + 32 j + lane % 32   of the T x T tile.
+    //                  and column  wc*WT + 32 j + lane % 32   of the T x T tile,
+    // i.e. four consecutive rows r0 .. r0 + 3 of one column c per (i, j, v / 4).
+    // The tile goes through LDS transposed, as E[c][r] = C[r][c]: each lane's
+    // four values are one 8-byte piece of a row of E.
     const float first_scale = args.first_iter ? args.scale[plan_idx] : 1.0f;
+    // T rows of 2 T bytes from global (row stride ld elements) into E, whole.
+    auto load_tile = [&](const uint16_t* src, int64_t ld) {
+        constexpr int kLoads = T * C::kERowBytes / 1024 / 4;  // 1 KB loads per wave
+        #pragma unroll 8
+        for (int i = 0; i < kLoads; ++i) {
+            const int q = wave * kLoads + i;
+            const int row = (1024 / C::kERowBytes) * q + lane / C::kEChunks;
+            const int lc = (lane % C::kEChunks) ^ swizzle_e<T>(row);
+            dma16(src + row * ld + lc * 8, lds_offset(smem + q * 1024));
+        }
+        wait_vm<0>();
+        __syncthreads();
+    };
+    // E row c, columns r .. r + 3 (r a multiple of 4)
+    auto e_ptr = [&](int c, int r) -> char* {
+        return smem + c * C::kERowBytes + (((r >> 3) ^ swizzle_e<T>(c)) << 4) + (r & 7) * 2;
+    };
+    // E rows to global rows (row stride ld elements), whole 16-byte chunks.
+    auto store_rows = [&](uint16_t* dst, int64_t ld) {
+        constexpr int kStores = T * C::kEChunks / 256;
+        #pragma unroll 8
+        for (int i = 0; i < kStores; ++i) {
+            const int q = tid + 256 * i;
+            const int row = q / C::kEChunks, lc = q % C::kEChunks;
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + row * C::kERowBytes +
+                                                            ((lc ^ swizzle_e<T>(row)) << 4));
+            *reinterpret_cast<uint4*>(dst + row * ld + lc * 8) = v;
+        }
+    };
+    // E columns to global rows: global row r gets E[c .. c + 7][r].  A
+    // transposing read of a 16-lane group takes rows c0 .. c0 + 3 of E at
+    // columns r0 .. r0 + 15 (source lane 4 k + q addresses row c0 + k, columns
+    // r0 + 4 q .. + 3) and hands lane i the four values E[c0 .. c0 + 3][r0 + i];
+    // two such reads give a lane 8 consecutive c of one r.  A wave covers 16
+    // rows r and 32 columns c per store, the 4 groups taking 8 columns each.
+    auto store_cols = [&](uint16_t* dst, int64_t ld) {
+        const int g = lane >> 4, i16 = lane & 15, k = i16 >> 2, q = i16 & 3;
+        constexpr int kRowBlocks = T / 16, kColBlocks = T / 32;
+        #pragma unroll 4
+        for (int it = 0; it < kRowBlocks * kColBlocks / 4; ++it) {
+            const int w = 4 * it + wave;
+            const int r0 = (w % kRowBlocks) * 16, cb = (w / kRowBlocks) * 32 + 8 * g;
+            shortx4 h[2];
+            #pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_shortx4*)((__attribute__((address_space(3))) char*)e_ptr(cb + 4 * hh + k, r0 + 4 * q)));
+            const shortx8 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            *reinterpret_cast<shortx8*>(dst + (int64_t)(r0 + i16) * ld + cb) = v;
+        }
+    };
+
+    __syncthreads();  // every wave is done with the last slab
     if (PHASE == kBX) {
         // Tile rows are long-side indices r, columns short-side indices c:
-        // X'[c][r] = s (a X[c][r] + acc[r][c]).  The X tile (T rows c, T
-        // columns r) goes through LDS: loaded whole, updated in place by each
-        // lane's own elements, stored whole.
-        constexpr int kERowBytes = 2 * T, kEChunks = T / 8;
+        // X'[c][r] = s (a X[c][r] + acc[r][c]); E is the X tile itself (T rows
+        // c, T columns r), loaded whole, updated in place, stored whole.
         const int64_t ldn = sg.n_pad;
         const uint16_t* Xs = P + (int64_t)J * T * ldn + (int64_t)I * T;
         uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.x_dst_off + slot * sg.x_stride) +
                        (int64_t)J * T * ldn + (int64_t)I * T;
-        __syncthreads();  // every wave is done with the last slab
-        constexpr int kLoads = T * kERowBytes / 1024 / 4;  // 1 KB loads per wave
-        #pragma unroll 8
-        for (int i = 0; i < kLoads; ++i) {
-            const int q = wave * kLoads + i;
-            const int row = (1024 / kERowBytes) * q + lane / kEChunks;
-            const int lc = (lane % kEChunks) ^ swizzle_e<T>(row);
-            __builtin_amdgcn_global_load_lds((gptr_t)(Xs + row * ldn + lc * 8), (lptr_t)(smem + q * 1024),
-                                             16, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        load_tile(Xs, ldn);
         const float a = args.a;
         #pragma unroll
         for (int i = 0; i < C::F; ++i)
@@ -394,9 +415,9 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
             for (int j = 0; j < C::F; ++j)
                 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4) {
-                    const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;  // long-side (column of X)
-                    const int c = wc * C::WT + j * 32 + lrow;                 // short-side (row of X)
-                    char* p = smem + c * kERowBytes + (((r0 >> 3) ^ swizzle_e<T>(c)) << 4) + (r0 & 7) * 2;
+                    const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
+                    const int c = wc * C::WT + j * 32 + lrow;
+                    char* p = e_ptr(c, r0);
                     const uint2 x = *reinterpret_cast<const uint2*>(p);
                     const float x0 = __uint_as_float(x.x << 16), x1 = __uint_as_float(x.x & 0xffff0000u);
                     const float x2 = __uint_as_float(x.y << 16), x3 = __uint_as_float(x.y & 0xffff0000u);
@@ -408,64 +429,56 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                     *reinterpret_cast<uint2*>(p) = o;
                 }
         __syncthreads();
-        constexpr int kStores = T * kEChunks / 256;
-        #pragma unroll 8
-        for (int i = 0; i < kStores; ++i) {
-            const int q = tid + 256 * i;
-            const int row = q / kEChunks, lc = q % kEChunks;
-            const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kERowBytes +
-                                                            ((lc ^ swizzle_e<T>(row)) << 4));
-            *reinterpret_cast<uint4*>(Xd + row * ldn + lc * 8) = v;
-        }
+        store_rows(Xd, ldn);
     } else {
+        // Out[I T + r][J T + c] = C[r][c] = E[c][r] and, off the diagonal, the
+        // mirror Out[J T + c][I T + r] = E[c][r].  E's rows are rows of block
+        // (J, I); on the diagonal that block is the tile itself (symmetric).
+        // The square's b A term reads A's block (J, I) = block (I, J)^T into E
+        // first (A is symmetric and stored whole).
         const int64_t ld = sg.m_pad;
         const int64_t out_off = PHASE == kGram ? sg.a_off + slot * sg.a_stride : sg.b_off + slot * sg.a_stride;
         uint16_t* Out = reinterpret_cast<uint16_t*>(args.ws + out_off);
-        const uint16_t* Ain = P;  // A, for the square phase's b A term
         const float alpha = PHASE == kGram ? first_scale * first_scale : args.c;
         const float beta = args.b;
-        const bool mirror = I != J;
+        if (PHASE == kSquare) load_tile(P + (int64_t)J * T * ld + (int64_t)I * T, ld);
         #pragma unroll
         for (int i = 0; i < C::F; ++i)
             #pragma unroll
             for (int j = 0; j < C::F; ++j)
                 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4) {
-                    const int64_t r0 = (int64_t)I * T + wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
-                    const int64_t c = (int64_t)J * T + wc * C::WT + j * 32 + lrow;
-                    uint16_t o[4];
+                    const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
+                    const int c = wc * C::WT + j * 32 + lrow;
+                    char* p = e_ptr(c, r0);
+                    float v[4];
                     #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int64_t e = (r0 + v) * ld + c;
-                        float val = alpha * acc[i][j][4 * v4 + v];
-                        if (PHASE == kSquare) val = fmaf(beta, bf16_to_f32(Ain[e]), val);
-                        o[v] = f32_to_bf16(val);
-                        Out[e] = o[v];
+                    for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * v4 + e];
+                    if (PHASE == kSquare) {
+                        const uint2 x = *reinterpret_cast<const uint2*>(p);
+                        v[0] = fmaf(beta, __uint_as_float(x.x << 16), v[0]);
+                        v[1] = fmaf(beta, __uint_as_float(x.x & 0xffff0000u), v[1]);
+                        v[2] = fmaf(beta, __uint_as_float(x.y << 16), v[2]);
+                        v[3] = fmaf(beta, __uint_as_float(x.y & 0xffff0000u), v[3]);
                     }
-                    if (mirror) {
-                        uint2 pk;
-                        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                        *reinterpret_cast<uint2*>(Out + c * ld + r0) = pk;
-                    }
+                    uint2 o;
+                    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(p) = o;
                 }
+        __syncthreads();
+        store_rows(Out + (int64_t)J * T * ld + (int64_t)I * T, ld);
+        if (I != J) store_cols(Out + (int64_t)I * T * ld + (int64_t)J * T, ld);
     }
 }
 
-// Pipeline depth per tile size.  A T = 256 stage is 64 KB with 64-wide slabs
-// (32 KB with 32-wide), a T = 128 stage a quarter of that.
-template <int T> struct Depth;
-template <> struct Depth<256> { static constexpr int S = DMUON_STAGES_256; };
-template <> struct Depth<128> { static constexpr int S = kBK == 32 ? 4 : 2; };
-
 template <int T>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
-    constexpr int S = Depth<T>::S;
     const dim3 grid((unsigned)a.total_blocks), block(256);
     switch (a.phase) {
-        case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram, S>), grid, block, 0, stream, a); break;
-        case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare, S>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX, S>), grid, block, 0, stream, a); break;
+        case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram>), grid, block, 0, stream, a); break;
+        case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX>), grid, block, 0, stream, a); break;
     }
     return hipGetLastError();
 }
