@@ -104,7 +104,8 @@ typedef struct dmuon_plan dmuon_plan; /* opaque, host memory only, immutable onc
  * members, descending, ties in order of first appearance; members keep input
  * order.  count == 0 gives an empty plan.  Errors: INVALID_ARG for count < 0,
  * descs == NULL with count > 0, out == NULL, a dim < 1 or an unknown dtype;
- * UNSUPPORTED for a dim >= 2^30; ALLOC on host allocation failure.
+ * UNSUPPORTED for a dim >= 2^30, or a side > 2^27 with a bf16 gradient; ALLOC
+ * on host allocation failure.
  * On success *out owns the plan; release it with muon_plan_destroy. */
 DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
 

@@ -17,6 +17,9 @@ constexpr int kPathBF16 = DMUON_BF16;
 // matrix; every tile granularity is a multiple of 64.
 constexpr int kPrepTile = 64;
 constexpr std::size_t kAlign = 256;
+// Longest side a bf16-gradient matrix may have: the bf16 kernels address up
+// to 8 rows of a slab with one 32-bit byte offset per lane.
+constexpr int64_t kMaxBf16Side = int64_t(1) << 27;
 
 inline std::size_t align_up(std::size_t x, std::size_t a = kAlign) { return (x + a - 1) / a * a; }
 

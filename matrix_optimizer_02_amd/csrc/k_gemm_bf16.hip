@@ -38,6 +38,9 @@
 #ifndef DMUON_SPREAD
 #define DMUON_SPREAD 1
 #endif
+#ifndef DMUON_ROTATE_K
+#define DMUON_ROTATE_K 1
+#endif
 
 namespace dmuon {
 namespace {
@@ -87,7 +90,12 @@ __device__ __forceinline__ void wait_vm() {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "m0", "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "m0", "memory");
+}
+// The same with a wave-uniform base address and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+                 : "m0", "memory");
 }
 #pragma clang diagnostic pop
 
@@ -171,27 +179,55 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     // ---- global -> LDS (direct) ----------------------------------------------------
     // One global_load_lds_dwordx4 of a wave fills 1 KB of LDS: lane l writes
     // bytes 16 l .. 16 l + 15 of it, so it fetches the global chunk that the
-    // swizzle places there.  Loads i0 .. i1-1 (of kDmaPerOp per operand) of
-    // the slab at k0 into the stage at dst.
+    // swizzle places there.  Load q (= wave kDmaPerOp + i) of an operand slab
+    // covers rows R q .. R q + R - 1 of it (R = 1 KB / row bytes), lane l row
+    // R q + l / (chunks per row); the address splits into a wave-uniform part
+    // (slab, q) and a per-lane part that depends on q only through the
+    // swizzle, i.e. through q's parity (kDmaPerOp is even).
+    //   K-contiguous rows (Gram, square P; every Q): R = 8, chunk swizzle
+    //   (l / 8) ^ (q & 1).
+    //   B X P slab (rows k of X): R = 2 (T = 256) or 4, chunk swizzle
+    //   swizzle_p of the row, whose two low bits hold 2 (q & 1) + l / 32 or l / 16.
+    static_assert(C::kDmaPerOp % 2 == 0, "load parity");
+    const int64_t p_row_ld = PHASE == kBX ? sg.n_pad : ldq;  // P slab row stride (elements)
+    uint32_t voff_p[2], voff_q[2];
+    #pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        if (PHASE == kBX) {
+            const int row = C::kPDmaRows * par + lane / C::kPChunks;
+            const int lc = (lane % C::kPChunks) ^ swizzle_p(row);
+            voff_p[par] = (uint32_t)(2 * ((lane / C::kPChunks) * p_row_ld + lc * 8));
+        } else {
+            const int lc = (lane % kChunks) ^ swizzle(kDmaRows * par + lane / kChunks);
+            voff_p[par] = (uint32_t)(2 * ((lane / kChunks) * p_row_ld + lc * 8));
+        }
+        const int lc = (lane % kChunks) ^ swizzle(kDmaRows * par + lane / kChunks);
+        voff_q[par] = (uint32_t)(2 * ((lane / kChunks) * ldq + lc * 8));
+    }
+    // wave-uniform byte addresses: P slab at k0 = p_base + k0 p_k + q p_q
+    const char* p_base = reinterpret_cast<const char*>(P) + (PHASE == kBX ? 2 * (int64_t)I * T : 2 * (int64_t)I * T * ldq);
+    const char* q_base = reinterpret_cast<const char*>(Qt);
+    const int64_t p_k = PHASE == kBX ? 2 * sg.n_pad : 2, p_q = PHASE == kBX ? 2 * C::kPDmaRows * sg.n_pad : 16 * ldq;
+    const int64_t q_q = 16 * ldq;
+    // The K loop starts right after the T-wide k range that the epilogue reads
+    // back (B X: X rows J T .., the tile's own X block; square: A columns
+    // I T .., the mirrored A block), so that range is loaded last and the
+    // epilogue finds it in L2.  K is a multiple of T.
+    int64_t k_rot = 0;
+    if (DMUON_ROTATE_K && PHASE != kGram) {
+        k_rot = (int64_t)((PHASE == kBX ? J : I) + 1) * T;
+        if (k_rot >= K) k_rot -= K;
+    }
+    // Loads i0 .. i1-1 (of kDmaPerOp per operand) of the slab at loop position
+    // k0 into the stage at dst.
     auto dma_part = [&](int64_t k0, char* dst, int i0, int i1) {
+        k0 += k_rot;
+        if (k0 >= K) k0 -= K;
         #pragma unroll
         for (int i = i0; i < i1; ++i) {
             const int q = wave * C::kDmaPerOp + i;  // 1 KB block of the operand slab
-            const uint16_t* gp;
-            if (PHASE == kBX) {
-                // P slab: X rows k0 .. k0 + kBK - 1, long-side columns I T .. I T + T - 1
-                const int row = C::kPDmaRows * q + lane / C::kPChunks;
-                const int lc = (lane % C::kPChunks) ^ swizzle_p(row);
-                gp = P + (k0 + row) * sg.n_pad + (int64_t)I * T + lc * 8;
-            } else {
-                const int row = kDmaRows * q + lane / kChunks;
-                const int lc = (lane % kChunks) ^ swizzle(row);
-                gp = P + ((int64_t)I * T + row) * ldq + k0 + lc * 8;
-            }
-            dma16(gp, lds_offset(dst + q * 1024));
-            const int qrow = kDmaRows * q + lane / kChunks;
-            const int qlc = (lane % kChunks) ^ swizzle(qrow);
-            dma16(Qt + (int64_t)qrow * ldq + k0 + qlc * 8, lds_offset(dst + C::kOperandBytes + q * 1024));
+            dma16(p_base + k0 * p_k + q * p_q, voff_p[i & 1], lds_offset(dst + q * 1024));
+            dma16(q_base + 2 * k0 + q * q_q, voff_q[i & 1], lds_offset(dst + C::kOperandBytes + q * 1024));
         }
     };
     // A slab's loads go out in three pieces: the first right after the barrier

@@ -41,6 +41,8 @@ extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count,
         if (d.rows < 1 || d.cols < 1 || !valid_dtype(d.grad_dtype) || !valid_dtype(d.param_dtype))
             return DMUON_ERR_INVALID_ARG;
         if (d.rows >= (int64_t(1) << 30) || d.cols >= (int64_t(1) << 30)) return DMUON_ERR_UNSUPPORTED;
+        // the bf16 kernels address a row stride with 32-bit lane offsets
+        if (d.grad_dtype == DMUON_BF16 && std::max(d.rows, d.cols) > kMaxBf16Side) return DMUON_ERR_UNSUPPORTED;
     }
     dmuon_plan* p = new (std::nothrow) dmuon_plan();
     if (p == nullptr) return DMUON_ERR_ALLOC;

@@ -95,6 +95,12 @@ def test_plan_errors():
     with pytest.raises(d.DMuonError) as e:
         d.Plan([(1 << 30, 5, 1, 1)])
     assert e.value.status == d.DMUON_ERR_UNSUPPORTED
+    # bf16 gradients: the long side is limited to 2^27; fp32 gradients are not
+    with pytest.raises(d.DMuonError) as e:
+        d.Plan([(5, (1 << 27) + 1, 1, 1)])
+    assert e.value.status == d.DMUON_ERR_UNSUPPORTED
+    d.Plan([(5, 1 << 27, 1, 1)]).close()
+    d.Plan([(5, (1 << 27) + 1, 0, 0)]).close()
     out = ctypes.c_void_p()
     assert LIB.muon_plan(None, 3, ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
     assert LIB.muon_plan(None, -1, ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
