@@ -29,11 +29,23 @@ __global__ void write_records_kernel(RecChunk c) {
     if (i < c.n) c.table[c.first + i] = c.rec[i];
 }
 
+// Sum of squares of four values, in one fixed order of explicit operations.
+__device__ __forceinline__ float sumsq4(float4 v) {
+    float s = v.x * v.x;
+    s = fmaf(v.y, v.y, s);
+    s = fmaf(v.z, v.z, s);
+    return fmaf(v.w, v.w, s);
+}
+
 // ---- prep ---------------------------------------------------------------------
 // One block per 64 x 64 tile of the padded stored-orientation matrix.  Thread
 // t covers columns 4 (t % 16) .. +3 of rows t / 16 + 16 p, p = 0..3.  X is
 // m_pad x n_pad: for a wide or square matrix it is U itself, for a tall one
 // U^T, written from the LDS copy of the tile so both sides stay coalesced.
+// The norm partials are taken in X's orientation -- each thread sums the
+// squares of the float4 groups it writes to X, and the partial of X tile
+// (i, j) sits at index i * (X tiles per row) + j -- so a tall matrix and its
+// transpose get bitwise the same norm.
 template <typename T, bool VEC>
 __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r, int64_t local,
                                           float (*tile)[kPrepTile + 1], float* red) {
@@ -93,9 +105,10 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
                 }
             }
         }
-        ss += u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + u[3] * u[3];
         if (!r.transposed) {
-            store4(X + rho * r.c_pad + kap, make_float4(u[0], u[1], u[2], u[3]));
+            const float4 v = make_float4(u[0], u[1], u[2], u[3]);
+            ss += sumsq4(v);
+            store4(X + rho * r.c_pad + kap, v);
         } else {
             #pragma unroll
             for (int q = 0; q < 4; ++q) tile[row][4 * cg + q] = u[q];
@@ -108,11 +121,14 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
             const int row_e = rr + 16 * p;  // column offset in the stored orientation
             const float4 v = make_float4(tile[4 * cg + 0][row_e], tile[4 * cg + 1][row_e],
                                          tile[4 * cg + 2][row_e], tile[4 * cg + 3][row_e]);
+            ss += sumsq4(v);
             store4(X + (kap0 + row_e) * r.r_pad + rho0 + 4 * cg, v);
         }
     }
     const float total = block_sum<kThreads>(ss, red);
-    if (t == 0) a.partials[r.partial_off + local] = total;
+    // X tile index: stored tile (rt, ct) is X tile (ct, rt) for a tall matrix
+    const int64_t xi = r.transposed ? (local % tiles_c) * (r.r_pad / kPrepTile) + local / tiles_c : local;
+    if (t == 0) a.partials[r.partial_off + xi] = total;
 }
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {

@@ -1,8 +1,10 @@
 // The three Newton-Schulz products on bf16 MFMA (gfx950), one grouped launch
 // per phase over every bucket of the batch:
 //   Gram    A  = s X X^T           upper-triangle tiles only, mirrored store
-//   square  B  = b A + c A A^T     (A A = A A^T: A is symmetric) upper tiles only
-//   BX      X' = s (a X + B X)     into the other X copy
+//   square  B' = a I + b A + c A A^T   (A A = A A^T: A is symmetric) upper tiles only
+//   BX      X' = s B' X            into the other X copy
+// X' = a X + B X is computed as (a I + B) X: the a X term rides on B's
+// diagonal, so the B X epilogue never reads X back.
 // s is 1 / (||U||_F + eps) in the first iteration (s^2 for the Gram) and 1
 // afterwards.  Each product is computed as C[i][j] = sum_k P[i][k] Q[j][k]:
 // for the Gram and square P = Q = X or A, whose rows are K-contiguous; for B X
@@ -37,6 +39,13 @@
 #endif
 #ifndef DMUON_SPREAD
 #define DMUON_SPREAD 1
+#endif
+// ends of the first and second load pieces, in eighths of a slab's loads
+#ifndef DMUON_PIECE1
+#define DMUON_PIECE1 3
+#endif
+#ifndef DMUON_PIECE2
+#define DMUON_PIECE2 6
 #endif
 #ifndef DMUON_ROTATE_K
 #define DMUON_ROTATE_K 1
@@ -209,13 +218,13 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     const char* q_base = reinterpret_cast<const char*>(Qt);
     const int64_t p_k = PHASE == kBX ? 2 * sg.n_pad : 2, p_q = PHASE == kBX ? 2 * C::kPDmaRows * sg.n_pad : 16 * ldq;
     const int64_t q_q = 16 * ldq;
-    // The K loop starts right after the T-wide k range that the epilogue reads
-    // back (B X: X rows J T .., the tile's own X block; square: A columns
-    // I T .., the mirrored A block), so that range is loaded last and the
-    // epilogue finds it in L2.  K is a multiple of T.
+    // The square's K loop starts right after the T-wide k range that its
+    // epilogue reads back (A columns I T .., the mirrored A block), so that
+    // range is loaded last and the epilogue finds it in L2.  K is a multiple
+    // of T.
     int64_t k_rot = 0;
-    if (DMUON_ROTATE_K && PHASE != kGram) {
-        k_rot = (int64_t)((PHASE == kBX ? J : I) + 1) * T;
+    if (DMUON_ROTATE_K && PHASE == kSquare) {
+        k_rot = (int64_t)(I + 1) * T;
         if (k_rot >= K) k_rot -= K;
     }
     // Loads i0 .. i1-1 (of kDmaPerOp per operand) of the slab at loop position
@@ -234,8 +243,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     // that frees its stage, the other two inside the next two k-steps, so the
     // address unit never takes a whole slab's loads at once while the matrix
     // pipe waits behind them.
-    constexpr int kPiece1 = DMUON_SPREAD ? (3 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
-    constexpr int kPiece2 = DMUON_SPREAD ? (6 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kPiece1 = DMUON_SPREAD ? (DMUON_PIECE1 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kPiece2 = DMUON_SPREAD ? (DMUON_PIECE2 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
 
     floatx16 acc[C::F][C::F];
     #pragma unroll
@@ -437,14 +446,10 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     __syncthreads();  // every wave is done with the last slab
     if (PHASE == kBX) {
         // Tile rows are long-side indices r, columns short-side indices c:
-        // X'[c][r] = s (a X[c][r] + acc[r][c]); E is the X tile itself (T rows
-        // c, T columns r), loaded whole, updated in place, stored whole.
+        // X'[c][r] = s acc[r][c]; E is the X' tile (T rows c, T columns r).
         const int64_t ldn = sg.n_pad;
-        const uint16_t* Xs = P + (int64_t)J * T * ldn + (int64_t)I * T;
         uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.x_dst_off + slot * sg.x_stride) +
                        (int64_t)J * T * ldn + (int64_t)I * T;
-        load_tile(Xs, ldn);
-        const float a = args.a;
         #pragma unroll
         for (int i = 0; i < C::F; ++i)
             #pragma unroll
@@ -453,16 +458,12 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                 for (int v4 = 0; v4 < 4; ++v4) {
                     const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
                     const int c = wc * C::WT + j * 32 + lrow;
-                    char* p = e_ptr(c, r0);
-                    const uint2 x = *reinterpret_cast<const uint2*>(p);
-                    const float x0 = __uint_as_float(x.x << 16), x1 = __uint_as_float(x.x & 0xffff0000u);
-                    const float x2 = __uint_as_float(x.y << 16), x3 = __uint_as_float(x.y & 0xffff0000u);
                     uint2 o;
-                    o.x = (uint32_t)f32_to_bf16(first_scale * fmaf(a, x0, acc[i][j][4 * v4 + 0])) |
-                          ((uint32_t)f32_to_bf16(first_scale * fmaf(a, x1, acc[i][j][4 * v4 + 1])) << 16);
-                    o.y = (uint32_t)f32_to_bf16(first_scale * fmaf(a, x2, acc[i][j][4 * v4 + 2])) |
-                          ((uint32_t)f32_to_bf16(first_scale * fmaf(a, x3, acc[i][j][4 * v4 + 3])) << 16);
-                    *reinterpret_cast<uint2*>(p) = o;
+                    o.x = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 0]) |
+                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 1]) << 16);
+                    o.y = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 2]) |
+                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 3]) << 16);
+                    *reinterpret_cast<uint2*>(e_ptr(c, r0)) = o;
                 }
         __syncthreads();
         store_rows(Xd, ldn);
@@ -496,6 +497,11 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
                         v[1] = fmaf(beta, __uint_as_float(x.x & 0xffff0000u), v[1]);
                         v[2] = fmaf(beta, __uint_as_float(x.y << 16), v[2]);
                         v[3] = fmaf(beta, __uint_as_float(x.y & 0xffff0000u), v[3]);
+                        if (I == J) {  // the a I term on the diagonal
+                            #pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (r0 + e == c) v[e] += args.a;
+                        }
                     }
                     uint2 o;
                     o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);

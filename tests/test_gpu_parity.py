@@ -235,13 +235,17 @@ def test_rank_one_and_diagonal_inputs():
         assert e < tol
 
 
-def test_transpose_bitwise():
-    # a tall matrix and its transpose run the same X in the same bucket layout:
-    # the outputs are exact transposes of each other
-    g = torch.randn(640, 256, device="cuda").to(torch.bfloat16)
-    say("case transpose ns_orthogonalize_batched")
-    o_tall, o_wide = orth_gpu([g, g.t().contiguous()])
-    assert torch.equal(o_tall, o_wide.t())
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_transpose_bitwise(seed):
+    # a tall matrix and its transpose run the same X in the same bucket layout,
+    # with the norm taken in X's orientation: the outputs are exact transposes
+    # of each other (ragged shapes included, both paths)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    for shape, dt in (((640, 256), torch.bfloat16), ((700, 300), torch.bfloat16), ((330, 130), torch.float32)):
+        g = torch.randn(shape, device="cuda", generator=gen).to(dt)
+        say(f"case transpose ns_orthogonalize_batched seed {seed} shape {shape} {dt}")
+        o_tall, o_wide = orth_gpu([g, g.t().contiguous()])
+        assert torch.equal(o_tall, o_wide.t())
 
 
 def test_batch_invariance_and_determinism():
