@@ -207,7 +207,7 @@ def main(argv=None):
         "matrices_per_s": round(w.count / step_s, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
         "gemm_ms_per_step": round(sum(gemm_ms) / len(per), 4),
-        "roofline": {"bound": "mfma", "kernel": "ns_gemm_bf16_kernel<256, BX> (X' = a X + B X)",
+        "roofline": {"bound": "mfma", "kernel": "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "launch_ms": round(bx_avg, 4), "flops_per_launch": bxf},
