@@ -20,3 +20,4 @@ from .muon_oracle import (  # noqa: F401
     round_to_f32,
 )
 from .plan_oracle import plan_reference, tile_granularity  # noqa: F401
+from .adamw_oracle import ADAMW_DEFAULTS, adamw_step  # noqa: F401
