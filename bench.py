@@ -13,8 +13,12 @@ of the whole step, sum over matrices of 5 (m(m+1)n + m(m+1)m + 2 m^2 n) flops
 (the Gram and A A^T triangles plus the dense B X product) divided by the step
 time.  ``roofline`` covers the dominant kernel, the B X product, timed live
 with HIP events at its launch boundaries inside the timed steps.
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+``elementwise`` gives the bandwidth-bound passes of the same steps (prep:
+momentum, cast and norm partials; apply: the update) in GB/s of their required
+traffic against the 8 TB/s HBM peak.  ``adamw`` times the AdamW companion
+step on Llama-3.1-8B's non-Muon parameters (one GPU's 1/8 element share) the
+same way.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+the same workload.
 """
 
 from __future__ import annotations
@@ -32,6 +36,7 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector/matrix
+HBM_PEAK_BPS = 8.0e12       # MI355X HBM3E
 NS_STEPS = 5
 LR, BETA, EPS = 0.02, 0.95, 1e-7
 
@@ -93,6 +98,31 @@ def cpu_baseline(w, host_samples):
             "seconds": dt}
 
 
+def adamw_bench(d, dev, steps: int = 10, warmup: int = 2):
+    """The AdamW companion step on Llama-3.1-8B's non-Muon share, timed with
+    HIP events on the current stream; bytes are the step's required traffic
+    (bf16 p and g, fp32 m and v: 22 bytes per element)."""
+    import torch
+
+    from matrix_optimizer_02_amd.workloads import ADAMW_LLAMA8B_SHARE, adamw_inputs
+
+    P, G, M, V = adamw_inputs(dev)
+    n = sum(p.numel() for p in P)
+    for t in range(warmup):
+        d.adamw_step_batched(P, G, M, V, step=10 + t)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(steps):
+        d.adamw_step_batched(P, G, M, V, step=10 + warmup + t)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = n * (2 + 2 + 4 + 4 + 2 + 4 + 4)
+    return {"workload": ADAMW_LLAMA8B_SHARE, "tensors": len(P), "elements": n, "ms": round(ms, 4),
+            "bytes": nbytes, "gbps": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms / 1e3) / HBM_PEAK_BPS, 4)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +130,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b_owner_1of8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW companion measurement")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times): the reference "
@@ -212,6 +243,22 @@ def main(argv=None):
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "launch_ms": round(bx_avg, 4), "flops_per_launch": bxf},
     }
+    # the bandwidth-bound passes of the same steps, against the HBM roofline
+    elems = w.elements()
+    gsz = 2 if paths == {"bf16"} else 4
+    psz = 2 if all(s.param_dtype == "bf16" for s in w.matrices) else 4
+    prep_bytes = elems * (gsz + 4 + 4 + gsz)   # read G, M; write M', U (as X)
+    apply_bytes = elems * (gsz + psz + psz)     # read O (X), W; write W'
+    out["elementwise"] = {
+        "prep": {"bytes": prep_bytes, "ms": round(avg["prep"], 4),
+                 "gbps": round(prep_bytes / (avg["prep"] / 1e3) / 1e9, 1),
+                 "frac_hbm": round(prep_bytes / (avg["prep"] / 1e3) / HBM_PEAK_BPS, 4)},
+        "apply": {"bytes": apply_bytes, "ms": round(avg["apply"], 4),
+                  "gbps": round(apply_bytes / (avg["apply"] / 1e3) / 1e9, 1),
+                  "frac_hbm": round(apply_bytes / (avg["apply"] / 1e3) / HBM_PEAK_BPS, 4)},
+    }
+    if not args.no_adamw:
+        out["adamw"] = adamw_bench(d, dev)
     if host_samples:
         out["cpu_baseline"] = cpu_baseline(w, host_samples)
     for e in events:

@@ -163,6 +163,39 @@ DMUON_API dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const vo
                                       float c, float eps, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ---- AdamW for the parameters that do not go through Muon -------------------
+ * The optimizer takes a separate AdamW learning rate for the parameters that
+ * its predicate does not route to Muon (DMuon project documentation,
+ * quick-start snippet and the VLA/VLM paragraph); the other hyper-parameters
+ * are the caller's.  step is the 1-based count of steps including this one. */
+typedef struct {
+    double lr;
+    double beta1, beta2; /* double: 1 - beta loses 3 digits in float (1 - (float)0.999 is off by 1.3e-5) */
+    double eps;
+    double weight_decay;
+    int64_t step;
+} dmuon_adamw_hparams;
+
+/* One AdamW step on each of `count` tensors, updated in place:
+ *   p <- p (1 - lr wd);  m <- beta1 m + (1 - beta1) g;  v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr m / (1 - beta1^step) / (sqrt(v / (1 - beta2^step)) + eps)
+ * Every array holds `count` entries (host arrays of device pointers):
+ * params[i] (param_dtypes[i]: DMUON_F32 | DMUON_BF16, stored rounded to nearest
+ * even) and grads[i] (grad_dtypes[i], read only) of numels[i] elements,
+ * exp_avgs[i] / exp_avg_sqs[i] fp32 moments of the same length.  Tensors are
+ * flat; numels[i] may be 0 (skipped).  The four buffers of a tensor are
+ * distinct and 16-byte aligned.  Arithmetic is fp32 on the device; 1 - beta,
+ * 1 - lr wd and the bias corrections are formed on the host in double and
+ * handed to the device rounded once to fp32.  Enqueued on `stream`;
+ * nothing is allocated.  Errors: INVALID_ARG (null or misaligned pointer,
+ * unknown dtype, negative numel, aliasing buffers, step < 1, beta outside
+ * [0, 1), eps <= 0, non-finite lr or weight decay), HIP. */
+DMUON_API dmuon_status adamw_step_batched(int32_t count, const int64_t* numels, const int32_t* param_dtypes,
+                                          const int32_t* grad_dtypes, void* const* params,
+                                          const void* const* grads, float* const* exp_avgs,
+                                          float* const* exp_avg_sqs, const dmuon_adamw_hparams* hp,
+                                          void* stream);
+
 /* ---- profiling ------------------------------------------------------------
  * The step of muon_step_batched, with a HIP event recorded on `stream` at each
  * phase boundary so that the caller can time every kernel phase live:

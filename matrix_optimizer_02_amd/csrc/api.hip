@@ -273,3 +273,65 @@ extern "C" dmuon_status dmuon_events_destroy(int32_t n, void** events) {
             st = DMUON_ERR_HIP;
     return st;
 }
+
+extern "C" dmuon_status adamw_step_batched(int32_t count, const int64_t* numels, const int32_t* param_dtypes,
+                                           const int32_t* grad_dtypes, void* const* params,
+                                           const void* const* grads, float* const* exp_avgs,
+                                           float* const* exp_avg_sqs, const dmuon_adamw_hparams* hp,
+                                           void* stream) {
+    if (count < 0 || hp == nullptr) return DMUON_ERR_INVALID_ARG;
+    if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) ||
+        !(hp->eps > 0.0) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+        return DMUON_ERR_INVALID_ARG;
+    if (count == 0) return DMUON_OK;
+    if (numels == nullptr || param_dtypes == nullptr || grad_dtypes == nullptr || params == nullptr ||
+        grads == nullptr || exp_avgs == nullptr || exp_avg_sqs == nullptr)
+        return DMUON_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < count; ++i) {
+        if (numels[i] < 0) return DMUON_ERR_INVALID_ARG;
+        const int32_t pd = param_dtypes[i], gd = grad_dtypes[i];
+        if ((pd != DMUON_F32 && pd != DMUON_BF16) || (gd != DMUON_F32 && gd != DMUON_BF16))
+            return DMUON_ERR_INVALID_ARG;
+        if (numels[i] == 0) continue;
+        if (!aligned16(params[i]) || !aligned16(grads[i]) || !aligned16(exp_avgs[i]) || !aligned16(exp_avg_sqs[i]))
+            return DMUON_ERR_INVALID_ARG;
+        const void* q[4] = {params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]};
+        for (int x = 0; x < 4; ++x)
+            for (int y = x + 1; y < 4; ++y)
+                if (q[x] == q[y]) return DMUON_ERR_INVALID_ARG;
+    }
+    // bias corrections in double on the host, handed to the kernel in fp32
+    const double t = (double)hp->step;
+    const double bc1 = 1.0 - std::pow(hp->beta1, t), bc2 = 1.0 - std::pow(hp->beta2, t);
+    AdamArgs a{};
+    a.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    a.beta1 = (float)hp->beta1;
+    a.one_minus_beta1 = (float)(1.0 - hp->beta1);
+    a.beta2 = (float)hp->beta2;
+    a.one_minus_beta2 = (float)(1.0 - hp->beta2);
+    a.step_size = (float)(hp->lr / bc1);
+    a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+    a.eps = (float)hp->eps;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t i = 0;
+    while (i < count) {
+        a.count = 0;
+        a.total_blocks = 0;
+        for (; i < count && a.count < kAdamChunk; ++i) {
+            if (numels[i] == 0) continue;
+            AdamRec& r = a.rec[a.count++];
+            r.p = params[i];
+            r.g = grads[i];
+            r.m = exp_avgs[i];
+            r.v = exp_avg_sqs[i];
+            r.n = numels[i];
+            r.block_begin = a.total_blocks;
+            r.p_dtype = param_dtypes[i];
+            r.g_dtype = grad_dtypes[i];
+            a.total_blocks += (numels[i] + kAdamBlock - 1) / kAdamBlock;
+        }
+        if (a.total_blocks > (int64_t)0x7fffffff) return DMUON_ERR_UNSUPPORTED;
+        if (launch_adamw(a, s) != hipSuccess) return DMUON_ERR_HIP;
+    }
+    return DMUON_OK;
+}

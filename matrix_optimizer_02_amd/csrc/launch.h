@@ -81,4 +81,32 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(int tile, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);
 
+// ---- AdamW for the non-Muon parameters (k_adamw.hip) ------------------------
+
+constexpr int kAdamBlock = 2048;  // elements per block
+constexpr int kAdamChunk = 64;    // tensors carried by one launch (kernel-argument table)
+
+struct AdamRec {
+    void* p;              // parameter (bf16 | fp32), updated in place
+    const void* g;        // gradient (bf16 | fp32)
+    float* m;             // first moment
+    float* v;             // second moment
+    int64_t n;            // elements (>= 1)
+    int64_t block_begin;  // first block of this tensor in the launch
+    int32_t p_dtype, g_dtype;
+};
+
+struct AdamArgs {
+    float decay;           // 1 - lr wd
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float step_size;       // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
+    float eps;
+    int32_t count;
+    int64_t total_blocks;
+    AdamRec rec[kAdamChunk];
+};
+
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t stream);
+
 }  // namespace dmuon

@@ -51,6 +51,11 @@ class HParams(ctypes.Structure):
                 ("ns_steps", ctypes.c_int32), ("nesterov", ctypes.c_int32)]
 
 
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built: run `python -m matrix_optimizer_02_amd.build`")
@@ -81,6 +86,8 @@ def _load():
         "dmuon_events_elapsed_ms": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.POINTER(ctypes.c_float)]),
         "dmuon_events_destroy": (ctypes.c_int, [ctypes.c_int32, vpp]),
+        "adamw_step_batched": (ctypes.c_int, [ctypes.c_int32, c_int64_p, c_int32_p, c_int32_p, vpp, vpp, vpp,
+                                              vpp, ctypes.POINTER(AdamWHParams), ctypes.c_void_p]),
         "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dmuon_version": (ctypes.c_char_p, []),
     }
@@ -275,6 +282,37 @@ def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs
                                        workspace.numel() * workspace.element_size(),
                                        _stream_handle(stream))
     _check(st, "ns_orthogonalize_batched")
+
+
+def adamw_step_batched(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                       exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor], *, step: int,
+                       lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.01,
+                       stream=None) -> None:
+    """Enqueue one AdamW step over a list of tensors (updated in place):
+    params bf16 or fp32, grads bf16 or fp32 of the same shape, fp32 moments.
+    ``step`` counts from 1 and includes this step."""
+    n = len(params)
+    if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have the same length")
+    for i in range(n):
+        p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+        for name, t in (("params", p), ("grads", g), ("exp_avgs", m), ("exp_avg_sqs", v)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}[{i}] must be a contiguous device tensor")
+        if not (p.numel() == g.numel() == m.numel() == v.numel()):
+            raise ValueError(f"tensor {i}: element counts differ")
+        if p.dtype not in _DTYPE_CODE or g.dtype not in _DTYPE_CODE:
+            raise ValueError(f"tensor {i}: params and grads must be float32 or bfloat16")
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise ValueError(f"tensor {i}: moments must be float32")
+    numels = (ctypes.c_int64 * max(1, n))(*[t.numel() for t in params])
+    pdt = (ctypes.c_int32 * max(1, n))(*[_DTYPE_CODE[t.dtype] for t in params])
+    gdt = (ctypes.c_int32 * max(1, n))(*[_DTYPE_CODE[t.dtype] for t in grads])
+    hp = AdamWHParams(lr, betas[0], betas[1], eps, weight_decay, int(step))
+    vp = ctypes.POINTER(ctypes.c_void_p)
+    arrs = [ctypes.cast(_ptr_array(x), vp) for x in (params, grads, exp_avgs, exp_avg_sqs)]
+    st = _lib.adamw_step_batched(n, numels, pdt, gdt, *arrs, ctypes.byref(hp), _stream_handle(stream))
+    _check(st, "adamw_step_batched")
 
 
 class PhaseEvents:

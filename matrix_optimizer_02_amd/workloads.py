@@ -230,3 +230,43 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, on_device_gen: bool = 
             else:
                 lst.append(host_tensor(w, i, kind, seed).to(device))
     return Gs, Ms, Ws
+
+
+# ---- AdamW companion: the parameters that do not go through Muon -------------------
+#
+# Llama-3.1-8B's non-projection parameters -- token embedding and LM head
+# (128256 x 4096 each, untied) and 65 RMSNorm weights of 4096 (two per layer
+# plus the final one) -- split evenly between 8 GPUs as element shards, the
+# way an element-wise optimizer's state is sharded.  One GPU's share: two
+# shards of 65 667 072 and 65 shards of 512 elements, bf16 parameters and
+# gradients, fp32 moments.  Parameters N(0, 0.02^2), gradients N(0, 1e-3^2),
+# first moments N(0, 1e-4^2), second moments the square of N(0, 1e-3^2), at
+# step 10.
+
+ADAMW_LLAMA8B_SHARE = "llama3.1-8b_adamw_share_1of8"
+
+
+def llama8b_adamw_share(owners: int = 8) -> List[tuple]:
+    """(name, numel) of one GPU's shard of each non-Muon tensor."""
+    vocab, hidden, layers = 128256, 4096, 32
+    out = [("embed", vocab * hidden // owners), ("lm_head", vocab * hidden // owners)]
+    out += [(f"norm{i}", hidden // owners) for i in range(2 * layers + 1)]
+    return out
+
+
+def adamw_inputs(device, seed: int = 0, owners: int = 8):
+    """Lists (params, grads, exp_avgs, exp_avg_sqs) of the AdamW share, generated
+    on ``device`` with torch's seeded generator, one key per (tensor, kind)."""
+    import torch
+
+    P, G, M, V = [], [], [], []
+    for idx, (_, n) in enumerate(llama8b_adamw_share(owners)):
+        def draw(kind, std):
+            gen = torch.Generator(device=device)
+            gen.manual_seed(_fold_seed((seed, 90, idx, kind)))
+            return torch.randn(n, generator=gen, dtype=torch.float32, device=device).mul_(std)
+        P.append(draw(PARAM, 0.02).to(torch.bfloat16))
+        G.append(draw(GRAD, 1e-3).to(torch.bfloat16))
+        M.append(draw(MOMENTUM, 1e-4))
+        V.append(draw(3, 1e-3).square_())
+    return P, G, M, V

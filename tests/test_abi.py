@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
                           "muon_plan_bucket", "muon_plan_destroy", "muon_step_batched",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
-                          "dmuon_status_string", "dmuon_version"}
+                          "adamw_step_batched", "dmuon_status_string", "dmuon_version"}
     for n in names:
         assert hasattr(raw, n), n
 
@@ -149,6 +149,36 @@ def test_step_argument_errors_before_device_work():
     assert ortho(p.handle, g, w, -1, 3.4445, -4.775, 2.0315, 1e-7, ws, ws_bytes, None) == d.DMUON_ERR_INVALID_ARG
     assert ortho(p.handle, g, g, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, ws_bytes, None) == d.DMUON_ERR_INVALID_ARG
     assert ortho(p.handle, g, w, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, 16, None) == d.DMUON_ERR_WORKSPACE
+
+
+@host_only
+def test_adamw_argument_errors_before_device_work():
+    # every call fails validation before any HIP call (fake addresses never dereferenced)
+    n = (ctypes.c_int64 * 2)(100, 8)
+    pd, gd = (ctypes.c_int32 * 2)(1, 0), (ctypes.c_int32 * 2)(1, 1)
+    P, G = _arr([0x10000, 0x20000]), _arr([0x30000, 0x40000])
+    M, V = _arr([0x50000, 0x60000]), _arr([0x70000, 0x80000])
+    hp = d.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    f = LIB.adamw_step_batched
+    E = d.DMUON_ERR_INVALID_ARG
+    assert f(-1, n, pd, gd, P, G, M, V, ctypes.byref(hp), None) == E
+    assert f(2, n, pd, gd, P, G, M, V, None, None) == E
+    assert f(2, None, pd, gd, P, G, M, V, ctypes.byref(hp), None) == E
+    assert f(2, n, pd, gd, P, None, M, V, ctypes.byref(hp), None) == E
+    for bad in (d.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0), d.AdamWHParams(1e-3, 1.0, 0.999, 1e-8, 0.01, 1),
+                d.AdamWHParams(1e-3, 0.9, -0.1, 1e-8, 0.01, 1), d.AdamWHParams(1e-3, 0.9, 0.999, 0.0, 0.01, 1),
+                d.AdamWHParams(float("nan"), 0.9, 0.999, 1e-8, 0.01, 1)):
+        assert f(2, n, pd, gd, P, G, M, V, ctypes.byref(bad), None) == E
+    assert f(2, n, (ctypes.c_int32 * 2)(1, 7), gd, P, G, M, V, ctypes.byref(hp), None) == E
+    assert f(2, (ctypes.c_int64 * 2)(100, -1), pd, gd, P, G, M, V, ctypes.byref(hp), None) == E
+    assert f(2, n, pd, gd, _arr([0x10004, 0x20000]), G, M, V, ctypes.byref(hp), None) == E  # misaligned
+    assert f(2, n, pd, gd, P, _arr([0x10000, 0x40000]), M, V, ctypes.byref(hp), None) == E  # g aliases p
+    assert f(2, n, pd, gd, P, G, M, _arr([0x50000, 0x80000]), ctypes.byref(hp), None) == E  # v aliases m
+    # count 0 and all-empty tensors enqueue nothing
+    assert f(0, None, None, None, None, None, None, None, ctypes.byref(hp), None) == d.DMUON_OK
+    z = (ctypes.c_int64 * 2)(0, 0)
+    assert f(2, z, pd, gd, _arr([0, 0]), _arr([0, 0]), _arr([0, 0]), _arr([0, 0]), ctypes.byref(hp),
+             None) == d.DMUON_OK
 
 
 def test_empty_plan_is_noop():
