@@ -292,17 +292,25 @@ def test_two_steps_and_checkpoint_restart():
         check_param(f64(W[i]), x1, r2, "bf16", "bf16", spec.rows, spec.cols)
 
 
-# ---- full size: the Llama-3.1-8B owner share, as timed by the benchmark --------------
+# ---- full size: the benchmark's owner share and the two full Qwen projection sets -----
+# One oracle sample per distinct (rows, cols), i.e. per shape and orientation.
 
-def test_full_size_owner_share_sampled():
-    w = get_workload("llama3.1-8b_owner_1of8")
-    say("case llama3.1-8b_owner_1of8 full muon_step_batched (28 matrices)")
-    G, M, W = make_inputs(w, "cuda", seed=0)
-    # one sample per distinct (rows, cols): k 1024x4096, q 4096^2, gate 14336x4096, down 4096x14336
+FULL_SETS = ["llama3.1-8b_owner_1of8", "qwen2.5-1.5b_proj", "qwen2.5-7b_proj"]
+
+
+def _samples(w):
     picks = {}
     for i, s in enumerate(w.matrices):
         picks.setdefault((s.rows, s.cols), i)
-    sample = sorted(picks.values())
+    return sorted(picks.values())
+
+
+@pytest.mark.parametrize("wname", FULL_SETS)
+def test_full_size_step_sampled(wname):
+    w = get_workload(wname)
+    say(f"case {wname} full muon_step_batched ({w.count} matrices, {w.elements()} elements)")
+    G, M, W = make_inputs(w, "cuda", seed=0)
+    sample = _samples(w)
     host = {i: (f64(G[i]), f64(M[i]), f64(W[i])) for i in sample}
     plan = d.plan_for(G, [x.dtype for x in W])
     ws = d.workspace_for(plan)
@@ -314,20 +322,22 @@ def test_full_size_owner_share_sampled():
         ref = oracle.muon_step(*host[i], lr=LR, beta=BETA, eps=EPS)
         assert rel(f64(M[i]), ref["M_new"]) < 1e-6
         check_param(f64(W[i]), host[i][2], ref, "bf16", "bf16", spec.rows, spec.cols)
+    del G, M, W, ws
+    torch.cuda.empty_cache()
 
 
-def test_full_size_owner_share_orthogonalize_sampled():
-    w = get_workload("llama3.1-8b_owner_1of8")
-    say("case llama3.1-8b_owner_1of8 full ns_orthogonalize_batched fp32 out")
+@pytest.mark.parametrize("wname", FULL_SETS)
+def test_full_size_orthogonalize_sampled(wname):
+    w = get_workload(wname)
+    say(f"case {wname} full ns_orthogonalize_batched bf16 in, fp32 out")
     G, _, _ = make_inputs(w, "cuda", seed=2)
     outs = orth_gpu(G)
-    picks = {}
-    for i, s in enumerate(w.matrices):
-        picks.setdefault((s.rows, s.cols), i)
-    for i in sorted(picks.values()):
+    for i in _samples(w):
         spec = w.matrices[i]
         say(f"  oracle sample {i} {spec.name} {spec.rows}x{spec.cols}")
         ref = oracle.newton_schulz(f64(G[i]), 5, A, B, C, EPS)
         e = rel(f64(outs[i]), ref)
         say(f"    rel err {e:.3e}")
         assert e < TOL["bf16"]
+    del G, outs
+    torch.cuda.empty_cache()
