@@ -31,8 +31,10 @@
 #include "launch.h"
 #include "tile_map.h"
 
+// which phases deal each XCD a contiguous run of a segment's tiles (bit per
+// phase: 1 Gram, 2 square, 4 B X); 0 keeps the hardware's round-robin
 #ifndef DMUON_XCD_REMAP
-#define DMUON_XCD_REMAP 0
+#define DMUON_XCD_REMAP 4
 #endif
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 
     // ---- which tile of which matrix --------------------------------------------
     int s, local;
-    if (DMUON_XCD_REMAP) {
+    if ((DMUON_XCD_REMAP >> PHASE) & 1) {
         xcd_map((int)blockIdx.x, args.nseg,
                 [&](int i) { return args.seg[i].count * args.seg[i].tiles_per_mat; },
                 [&](int i) { return args.seg[i].first_block; }, s, local);

@@ -9,6 +9,7 @@ product path.
 from .muon_oracle import (  # noqa: F401
     NS_COEFFS,
     frobenius_normalize,
+    gram_newton_schulz,
     momentum,
     muon_step,
     newton_schulz,

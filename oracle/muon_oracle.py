@@ -118,6 +118,36 @@ def newton_schulz(G, steps: int, a: float = NS_COEFFS[0], b: float = NS_COEFFS[1
     return X.T.copy() if transposed else X
 
 
+def gram_newton_schulz(G, steps: int, a: float = NS_COEFFS[0], b: float = NS_COEFFS[1],
+                       c: float = NS_COEFFS[2], eps: float = 1e-7):
+    """The same map as ``newton_schulz``, run as the m x m Gram-space recurrence
+    (explainer, second section 2.1: the iteration moves into the Gram space of
+    the short side, lowering its cost from order m^2 n to order m^3).
+
+    Every iterate of the short-side recurrence is X_k = P_k X_0 with P_0 = I.
+    Writing A_k = X_k X_k^T = P_k A_0 P_k^T and Q_k = a I + b A_k + c A_k A_k,
+    the step X_{k+1} = Q_k X_k becomes P_{k+1} = Q_k P_k and
+    A_{k+1} = Q_k A_k Q_k^T; the result is O = P_steps X_0.  Dense fp64, no
+    symmetry tricks; a tall G is transposed before and after, as there.
+    """
+    X = _f64(G)
+    if X.ndim != 2:
+        raise ValueError("gram_newton_schulz expects a 2-D matrix")
+    transposed = X.shape[0] > X.shape[1]
+    if transposed:
+        X = X.T.copy()
+    X0 = frobenius_normalize(X, eps)
+    m = X0.shape[0]
+    A = X0 @ X0.T
+    P = np.eye(m)
+    for _ in range(int(steps)):
+        Q = a * np.eye(m) + b * A + c * (A @ A)
+        P = Q @ P
+        A = Q @ A @ Q.T
+    O = P @ X0
+    return O.T.copy() if transposed else O
+
+
 def update_scale(rows: int, cols: int) -> float:
     """Per-matrix update scale s = sqrt(max(1, rows / cols)) of the stored
     (out x in) parameter: tall matrices get s > 1, wide and square ones s = 1."""

@@ -13,6 +13,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+import oracle
+
 from oracle import (NS_COEFFS, apply_update, frobenius_normalize, momentum, muon_step,
                     newton_schulz, ns_cost, round_to_bf16, update_scale)
 
@@ -321,3 +323,20 @@ def test_bf16_rounding_ties_and_library():
     x = x.astype(np.float32).astype(np.float64)  # torch rounds from fp32
     want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(round_to_bf16(x), want)
+
+
+@pytest.mark.parametrize("shape", [(12, 40), (40, 12), (16, 16), (7, 9)])
+@pytest.mark.parametrize("steps", [0, 1, 2, 5])
+def test_gram_space_recurrence_matches_definition(shape, steps):
+    # the Gram-space recurrence reaches the short-side iteration's result exactly
+    # (up to fp64 rounding), and both match the SVD closed form
+    rng = np.random.default_rng(sum(shape) + steps)
+    G = rng.standard_normal(shape)
+    ref = oracle.newton_schulz(G, steps)
+    got = oracle.gram_newton_schulz(G, steps)
+    assert np.linalg.norm(got - ref) <= 1e-12 * max(np.linalg.norm(ref), 1.0)
+    u, sv, vt = np.linalg.svd(G, full_matrices=False)
+    x = sv / (np.linalg.norm(G) + 1e-7)
+    for _ in range(steps):
+        x = A_ * x + B_ * x ** 3 + C_ * x ** 5
+    assert np.linalg.norm(got - (u * x) @ vt) <= 1e-11 * max(np.linalg.norm(got), 1.0)
