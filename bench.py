@@ -9,10 +9,16 @@ default workload is the Llama-3.1-8B projection set's owner share (one of 8 LPT
 owners: 28 matrices, bf16 gradients and parameters, fp32 momentum).
 
 Printed: one JSON line.  ``value`` is the algorithmic Newton-Schulz throughput
-of the whole step, sum over matrices of 5 (m(m+1)n + m(m+1)m + 2 m^2 n) flops
-(the Gram and A A^T triangles plus the dense B X product) divided by the step
-time.  ``roofline`` covers the dominant kernel, the B X product, timed live
-with HIP events at its launch boundaries inside the timed steps.
+of the whole step: the short-side recurrence's flops, summed over matrices as
+5 (m(m+1)n + m(m+1)m + 2 m^2 n) (the Gram and A A^T triangles plus the dense
+B X product), divided by the step time -- a fixed amount of work per workload,
+so ``value`` moves with 1 / step time whichever form of the recurrence runs.
+``executed_tflops`` and ``pct_bf16_peak`` count the flops the library actually
+performs (fewer for buckets that run the Gram-space form: 6 m^2 n + 14 m^3
+over 5 iterations with a restart after 3, triangles halved), i.e. the
+matrix-core utilisation.
+``roofline`` covers the dominant kernel, the B X product, timed live with HIP
+events at its launch boundaries inside the timed steps.
 ``elementwise`` gives the bandwidth-bound passes of the same steps (prep:
 momentum, cast and norm partials; apply: the update) in GB/s of their required
 traffic against the 8 TB/s HBM peak.  ``adamw`` times the AdamW companion
@@ -52,6 +58,23 @@ def dense_flops(m: int, n: int) -> int:
 
 def bx_flops(m: int, n: int) -> int:
     return 2 * m * m * n
+
+
+def executed_flops(m: int, n: int, seg_len: int, steps: int = NS_STEPS) -> dict:
+    """Flops one matrix's iterations perform, per phase kind, on the real
+    shape with triangles halved as the kernels compute them.  The iterations
+    run as segments of seg_len (1: the short side; the last segment shorter);
+    a segment of L iterations takes one Gram product, L squares, 3 (L - 1)
+    m x m triangles (P' = Q P, T = A Q, A' = Q T) and one B X product."""
+    tri_n, tri_m = m * (m + 1) * n, m * (m + 1) * m
+    segs = [seg_len] * (steps // seg_len) + ([steps % seg_len] if steps % seg_len else [])
+    out = {"gram": 0, "square": 0, "prod": 0, "bx": 0}
+    for L in segs:
+        out["gram"] += tri_n
+        out["square"] += L * tri_m
+        out["prod"] += 3 * (L - 1) * tri_m
+        out["bx"] += bx_flops(m, n)
+    return out
 
 
 def read_traffic(kernel_tag: str):
@@ -202,20 +225,32 @@ def main(argv=None):
     names = events[0].names()
     per = [e.elapsed_ms() for e in events]
     avg = {nm: sum(p[j] for p in per) / len(per) for j, nm in enumerate(names)}
-    bx_ms = [p[j] for p in per for j, nm in enumerate(names) if nm.startswith("bx")]
-    gemm_ms = [p[j] for p in per for j, nm in enumerate(names) if nm[:-1] in ("gram", "square", "bx")]
-    bx_avg = sum(bx_ms) / len(bx_ms)
+    kind_of = lambda nm: re.sub(r"\d+$", "", nm)
+    gemm_ms = [p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) in ("gram", "square", "prod", "bx")]
 
-    alg = dense = bxf = 0
-    for s in w.matrices:
+    # the recurrence form the plan picked for each matrix's bucket (iterations per segment)
+    seg_len = [plan.bucket(plan.query(i).bucket).gram_restart for i in range(w.count)]
+    gram_space = [plan.bucket(plan.query(i).bucket).algo == d.ALGO_GRAM_SPACE for i in range(w.count)]
+    alg = dense = 0
+    execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}
+    for s, L in zip(w.matrices, seg_len):
         m, n = min(s.rows, s.cols), max(s.rows, s.cols)
         alg += NS_STEPS * algorithmic_flops(m, n)
         dense += NS_STEPS * dense_flops(m, n)
-        bxf += bx_flops(m, n)
+        for k, v in executed_flops(m, n, L).items():
+            execd[k] += v
+    executed = sum(execd.values())
     step_s = ms_per_step / 1e3
     value = alg / step_s / 1e12
     peak = BF16_PEAK_TFLOPS if paths == {"bf16"} else FP32_PEAK_TFLOPS
+    # B X phases that launch anything: iteration k closes a segment of some bucket
+    bx_iters = [k for k in range(NS_STEPS) if any(k % L == L - 1 or k == NS_STEPS - 1 for L in set(seg_len))]
+    bx_ms = [p[names.index(f"bx{k}")] for p in per for k in bx_iters]
+    bx_avg = sum(bx_ms) / len(bx_ms)
+    bxf = execd["bx"] / len(bx_iters)  # per B X phase (one grouped launch per tile class)
     achieved = bxf / (bx_avg / 1e3) / 1e12
+    phase_tot = {k: sum(p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) == k) / len(per)
+                 for k in execd}
     traffic = read_traffic("bx_gemm_bf16_llama8b") if args.workload == "llama3.1-8b_owner_1of8" else None
 
     out = {
@@ -233,8 +268,14 @@ def main(argv=None):
         "data": "synthetic (seeded normal gradients, momenta and parameters)",
         "config": {"workload": w.name, "matrices": w.count, "elements": w.elements(),
                    "ns_steps": NS_STEPS, "lr": LR, "beta": BETA, "nesterov": True},
-        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 3),
+        "executed_tflops": round(executed / step_s / 1e12, 3),
+        "pct_bf16_peak": round(100.0 * executed / step_s / 1e12 / BF16_PEAK_TFLOPS, 3),
         "ns_tflops_dense_equiv": round(dense / step_s / 1e12, 3),
+        "recurrence": {"gram_space_matrices": sum(gram_space), "short_side_matrices": w.count - sum(gram_space),
+                       "gram_restart": max(seg_len) if any(gram_space) else None},
+        "gemm_phases": {k: {"ms": round(phase_tot[k], 4), "executed_flops": execd[k],
+                            "tflops": round(execd[k] / (phase_tot[k] / 1e3) / 1e12, 1) if phase_tot[k] > 0 else None}
+                        for k in execd},
         "matrices_per_s": round(w.count / step_s, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
         "gemm_ms_per_step": round(sum(gemm_ms) / len(per), 4),

@@ -94,6 +94,38 @@ typedef struct {
 
 typedef struct dmuon_plan dmuon_plan; /* opaque, host memory only, immutable once built */
 
+/* How a bucket runs its Newton-Schulz iterations. */
+typedef enum {
+    DMUON_ALGO_AUTO = 0,  /* plan option: Gram space where it saves work, else short side */
+    DMUON_ALGO_SHORT_SIDE = 1,
+    /* The iteration carried in the m x m Gram space (DMuon explainer on
+     * gist.science, second section 2.1 Efficiente Gram Newton-Schulz
+     * Iteratie): X_k = P_k X_0 with A_0 = X_0 X_0^T and, per iteration,
+     * Q = a I + b A + c A A, P <- Q P, A <- Q A Q.  All of these are
+     * polynomials in A_0, hence symmetric and commuting, and each product is
+     * computed on one triangle.  Every gram_restart iterations (and after the
+     * last) the recurrence restarts from the actual iterate X = P X_0 with a
+     * fresh Gram matrix X X^T: with A's rounding amplified by P^2 along
+     * directions that X_0 barely spans, the Gram space in bf16 resolves small
+     * singular values far worse than the short side, and restarts bound that
+     * loss.  A segment of L iterations costs 3 m^2 n + (4 L - 3) m^3 flops
+     * (the short side: 3 m^2 n + m^3 per iteration), so 5 iterations as 3 + 2
+     * take 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3: cheaper whenever n > m. */
+    DMUON_ALGO_GRAM_SPACE = 2
+} dmuon_algo;
+
+typedef struct {
+    int32_t algo;         /* dmuon_algo; DMUON_ALGO_AUTO (the default) picks the Gram space for
+                             bf16 buckets with padded n > padded m whose members all have
+                             n >= 1.5 m, else the short side;
+                             DMUON_ALGO_GRAM_SPACE forces it on every bf16 bucket;
+                             DMUON_ALGO_SHORT_SIDE forces the short side everywhere.  fp32
+                             buckets always run the short side. */
+    int32_t gram_restart; /* Gram-space iterations between restarts, >= 1; 0: the default, 3.
+                             Larger values save m^2 n work and lose accuracy on
+                             ill-conditioned inputs; 1 is the short side. */
+} dmuon_plan_opts;
+
 /* Build the batch plan (host only, no device work).  Per matrix: m = min(rows,
  * cols), n = max(rows, cols), transposed = rows > cols (square matrices are
  * not transposed).  Tile granularity g = 64 on the fp32 path; on the bf16 path
@@ -109,9 +141,15 @@ typedef struct dmuon_plan dmuon_plan; /* opaque, host memory only, immutable onc
  * On success *out owns the plan; release it with muon_plan_destroy. */
 DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
 
+/* muon_plan with options (opts == NULL: the defaults).  INVALID_ARG also for
+ * an unknown opts->algo or opts->gram_restart < 0. */
+DMUON_API dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t count, const dmuon_plan_opts* opts,
+                                    dmuon_plan** out);
+
 /* Bytes of device workspace a step or orthogonalisation with this plan needs
  * (0 for an empty plan).  The workspace holds the per-bucket X (two copies),
- * A and B operands, per-matrix norms and a small descriptor table;
+ * A and B operands (and, for Gram-space buckets, three more m x m matrices
+ * per member), per-matrix norms and a small descriptor table;
  * its contents need no initialisation and are garbage after a call. */
 DMUON_API dmuon_status muon_plan_workspace_bytes(const dmuon_plan* plan, size_t* bytes);
 
@@ -131,6 +169,15 @@ DMUON_API dmuon_status muon_plan_query(const dmuon_plan* plan, int32_t idx, int3
 DMUON_API dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket, int32_t* path,
                               int64_t* padded_m, int64_t* padded_n, int32_t* count,
                               int32_t* tile);
+
+/* The dmuon_algo a bucket runs (DMUON_ALGO_SHORT_SIDE or DMUON_ALGO_GRAM_SPACE) and its
+ * iterations per Gram-space segment (1 on the short side).  A call with ns_steps
+ * iterations runs Gram-space buckets as segments of gram_restart iterations, the
+ * last one shorter if needed; if |a|^gram_restart > 2^64 (P grows like a^k along
+ * directions that X_0 barely spans) the call runs them on the short side instead.
+ * Either pointer may be NULL. */
+DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bucket, int32_t* algo,
+                                             int32_t* gram_restart);
 
 /* Release a plan (NULL is a no-op). */
 DMUON_API void muon_plan_destroy(dmuon_plan* plan);
@@ -200,9 +247,12 @@ DMUON_API dmuon_status adamw_step_batched(int32_t count, const int64_t* numels, 
  * The step of muon_step_batched, with a HIP event recorded on `stream` at each
  * phase boundary so that the caller can time every kernel phase live:
  * events[0] before the first launch, then one event after each phase, the
- * phases being: prep (momentum, cast, norms), then for every iteration the
- * Gram, square and BX products (each one grouped launch per tile class), then
- * the update.  Needs num_events >= muon_step_event_count(hp->ns_steps)
+ * phases being: prep (momentum, cast, norms), then for every iteration four
+ * phases -- Gram (short-side buckets; Gram-space buckets in the first
+ * iteration only), square (every bucket), products (the Gram-space buckets'
+ * P and A updates), B X (short-side buckets; Gram-space buckets' O = P X_0 in
+ * the last iteration) -- each a set of grouped launches, some possibly empty,
+ * then the update.  Needs num_events >= muon_step_event_count(hp->ns_steps)
  * event handles (hipEvent_t, e.g. from dmuon_events_create); nothing is
  * synchronised.  Errors as for muon_step_batched, INVALID_ARG for too few or
  * NULL events. */
@@ -212,7 +262,7 @@ DMUON_API dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const 
                                                   size_t workspace_bytes, void* stream,
                                                   void* const* events, int32_t num_events);
 
-/* Events muon_step_batched_profiled records: 3 + 3 ns_steps (-1 if ns_steps < 0). */
+/* Events muon_step_batched_profiled records: 3 + 4 ns_steps (-1 if ns_steps < 0). */
 DMUON_API int32_t muon_step_event_count(int32_t ns_steps);
 
 /* Create n HIP events (timing enabled) into events[0..n); the caller destroys

@@ -1,12 +1,15 @@
 // C-ABI entry points of libdmuon_ns that enqueue device work: argument checks,
 // the per-call matrix table, and the launch sequence of one step
 //   records -> prep (momentum, U, X, norm partials) -> norms
-//   -> ns_steps x (Gram, square, BX), each one grouped launch per tile class
+//   -> ns_steps x (Gram, square, prod, BX), each phase a grouped launch per
+//      tile class (prod: two, for the Gram-space buckets)
 //   -> apply (update or output).
 // No device memory is allocated and nothing is synchronised: everything is
 // enqueued on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "dmuon_internal.h"
@@ -49,8 +52,17 @@ struct TileClass {
 };
 constexpr TileClass kClasses[] = {{kPathBF16, 256}, {kPathBF16, 128}, {kPathF32, 64}};
 
-hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const StepParams& sp,
-                        int iter, int phase, hipStream_t stream) {
+// One bucket's product in a grouped launch: operand and output arrays as
+// bucket base byte offsets in the workspace.
+struct SegSpec {
+    const BucketPlan* bp;
+    int64_t p_off, q_off, o_off;
+    int32_t first_iter;
+};
+
+// One grouped launch per tile class over the given products of one phase.
+hipError_t launch_segs(char* ws, const float* scale, const StepParams& sp, int phase,
+                       const std::vector<SegSpec>& segs, hipStream_t stream) {
     for (const TileClass& tc : kClasses) {
         GemmArgs ga{};
         ga.ws = ws;
@@ -59,7 +71,6 @@ hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const
         ga.b = sp.b;
         ga.c = sp.c;
         ga.phase = phase;
-        ga.first_iter = iter == 0 ? 1 : 0;
         auto flush = [&]() -> hipError_t {
             if (ga.nseg == 0) return hipSuccess;
             hipError_t e = tc.path == kPathBF16 ? launch_gemm_bf16(tc.tile, ga, stream)
@@ -68,7 +79,8 @@ hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const
             ga.total_blocks = 0;
             return e;
         };
-        for (const BucketPlan& bp : p->buckets) {
+        for (const SegSpec& ss : segs) {
+            const BucketPlan& bp = *ss.bp;
             if (bp.path != tc.path || bp.tile != tc.tile) continue;
             if (ga.nseg == kMaxSeg) {
                 hipError_t e = flush();
@@ -80,13 +92,13 @@ hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const
             s.tiles_per_mat = phase == kBX ? s.tm * s.tn : s.tm * (s.tm + 1) / 2;
             s.count = (int32_t)bp.members.size();
             s.plan_base = bp.plan_base;
+            s.first_iter = ss.first_iter;
             s.first_block = ga.total_blocks;
             s.m_pad = bp.m_pad;
             s.n_pad = bp.n_pad;
-            s.x_src_off = (int64_t)(iter % 2 == 0 ? bp.off_x0 : bp.off_x1);
-            s.x_dst_off = (int64_t)(iter % 2 == 0 ? bp.off_x1 : bp.off_x0);
-            s.a_off = (int64_t)bp.off_a;
-            s.b_off = (int64_t)bp.off_b;
+            s.p_off = ss.p_off;
+            s.q_off = ss.q_off;
+            s.o_off = ss.o_off;
             s.x_stride = bp.m_pad * bp.n_pad * bp.esize;
             s.a_stride = bp.m_pad * bp.m_pad * bp.esize;
             ga.total_blocks += s.count * s.tiles_per_mat;
@@ -97,9 +109,26 @@ hipError_t launch_phase(const dmuon_plan* p, char* ws, const float* scale, const
     return hipSuccess;
 }
 
+// A bucket's m x m arrays (bucket base offsets) in their current roles: A_j,
+// Q_j, P_j, the next P and the product T = A_j Q_j.  Short-side buckets only
+// ever use the first two (A and B); Gram-space buckets rotate the five.
+struct Roles {
+    int64_t a, q, p, p2, t;
+};
+
+// Iterations per segment that this call runs a bucket with.  Along directions
+// that X_0 barely spans, P grows like a^j within a segment; beyond 2^64 the
+// call runs the bucket on the short side instead.
+int32_t seg_len_for(const BucketPlan& bp, const StepParams& sp) {
+    if (bp.seg_len <= 1) return 1;
+    const double growth = (double)bp.seg_len * std::log2(std::max(1.0, (double)std::fabs(sp.a)));
+    return growth <= 64.0 ? bp.seg_len : 1;
+}
+
 // events == nullptr: plain run.  Otherwise events[0] is recorded before the
 // first launch and events[1 + k] after phase k, phases being: prep (records,
-// momentum/cast, norms), then per iteration Gram, square, BX, then apply.
+// momentum/cast, norms), then per iteration Gram, square, prod, BX (each
+// possibly empty), then apply.
 dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
                  void* const* events = nullptr) {
     const int32_t count = (int32_t)p->mats.size();
@@ -114,6 +143,10 @@ dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hip
     DevMatRec* table = reinterpret_cast<DevMatRec*>(ws + p->off_records);
     float* scale = reinterpret_cast<float*>(ws + p->off_scale);
     float* partials = reinterpret_cast<float*>(ws + p->off_partials);
+    const int steps = sp.ns_steps;
+    const size_t nb = p->buckets.size();
+    std::vector<int32_t> seg(nb);
+    for (size_t b = 0; b < nb; ++b) seg[b] = seg_len_for(p->buckets[b], sp);
 
     // per-matrix records, plan order, written into the workspace by small launches
     RecChunk chunk{};
@@ -144,6 +177,9 @@ dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hip
         r.dst_dtype = mp.param_dtype;
         r.path = bp.path;
         r.upd_scale = (float)std::sqrt(std::max(1.0, (double)mp.rows / (double)mp.cols));
+        // every segment's closing product moves X into the other copy
+        const int32_t L = seg[mp.bucket];
+        r.final_copy = ((steps + L - 1) / L) % 2;
         chunk.rec[chunk.n++] = r;
         if (chunk.n == kRecChunk || pi == count - 1) {
             if (launch_write_records(chunk, stream) != hipSuccess) return DMUON_ERR_HIP;
@@ -166,19 +202,80 @@ dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hip
         return DMUON_ERR_HIP;
     if (!mark()) return DMUON_ERR_HIP;
 
-    for (int it = 0; it < sp.ns_steps; ++it)
-        for (int phase : {kGram, kSquare, kBX}) {
-            if (launch_phase(p, ws, scale, sp, it, phase, stream) != hipSuccess) return DMUON_ERR_HIP;
-            if (!mark()) return DMUON_ERR_HIP;
+    // The iterations as segments of seg[b] iterations per bucket (1: the
+    // short side).  Iteration k is position j = k mod L of its segment, whose
+    // length Lc is L, or less for the last one.  A segment takes
+    //   j = 0:      A = s^2 X X^T from the current X copy (s: first segment only)
+    //   every j:    Q_j = a I + b A + c A A
+    //   j >= 1:     P_{j+1} = Q_j P_j            (P_1 = Q_0)
+    //   j < Lc - 1: T = A Q_j, then A = Q_j T
+    //   j = Lc - 1: X' = s P_Lc X into the other X copy
+    // so a segment of one iteration is exactly the short-side iteration.
+    std::vector<Roles> roles(nb);
+    std::vector<int32_t> xcur(nb, 0);  // X copy holding the current iterate
+    for (size_t b = 0; b < nb; ++b) {
+        const BucketPlan& bp = p->buckets[b];
+        roles[b] = Roles{(int64_t)bp.off_a, (int64_t)bp.off_b, (int64_t)bp.off_g[0], (int64_t)bp.off_g[1],
+                         (int64_t)bp.off_g[2]};
+    }
+    auto xoff = [&](size_t b, int copy) {
+        return (int64_t)(copy == 0 ? p->buckets[b].off_x0 : p->buckets[b].off_x1);
+    };
+    std::vector<SegSpec> segs;
+    segs.reserve(2 * nb);
+    auto phase_done = [&](int phase) -> bool {
+        const bool ok = launch_segs(ws, scale, sp, phase, segs, stream) == hipSuccess;
+        segs.clear();
+        return ok;
+    };
+    for (int it = 0; it < steps; ++it) {
+        std::vector<int32_t> j(nb), lc(nb);
+        for (size_t b = 0; b < nb; ++b) {
+            j[b] = it % seg[b];
+            lc[b] = std::min(seg[b], steps - (it - j[b]));
         }
+        for (size_t b = 0; b < nb; ++b)
+            if (j[b] == 0) segs.push_back({&p->buckets[b], xoff(b, xcur[b]), 0, roles[b].a, it == 0 ? 1 : 0});
+        if (!phase_done(kGram) || !mark()) return DMUON_ERR_HIP;
+
+        for (size_t b = 0; b < nb; ++b) segs.push_back({&p->buckets[b], roles[b].a, 0, roles[b].q, 0});
+        if (!phase_done(kSquare) || !mark()) return DMUON_ERR_HIP;
+
+        for (size_t b = 0; b < nb; ++b) {
+            const Roles& r = roles[b];
+            if (j[b] >= 1) segs.push_back({&p->buckets[b], r.q, r.p, r.p2, 0});
+            if (j[b] < lc[b] - 1) segs.push_back({&p->buckets[b], r.a, r.q, r.t, 0});
+        }
+        if (!phase_done(kProd)) return DMUON_ERR_HIP;
+        for (size_t b = 0; b < nb; ++b)
+            if (j[b] < lc[b] - 1) segs.push_back({&p->buckets[b], roles[b].q, roles[b].t, roles[b].a, 0});
+        if (!phase_done(kProd) || !mark()) return DMUON_ERR_HIP;
+
+        for (size_t b = 0; b < nb; ++b) {
+            if (j[b] != lc[b] - 1) continue;
+            const int64_t pfin = j[b] == 0 ? roles[b].q : roles[b].p2;  // P_Lc
+            segs.push_back({&p->buckets[b], xoff(b, xcur[b]), pfin, xoff(b, 1 - xcur[b]), it == j[b] ? 1 : 0});
+        }
+        if (!phase_done(kBX) || !mark()) return DMUON_ERR_HIP;
+
+        for (size_t b = 0; b < nb; ++b) {
+            Roles& r = roles[b];
+            if (j[b] == lc[b] - 1) {
+                xcur[b] = 1 - xcur[b];  // segment closed; its arrays are free again
+            } else if (j[b] == 0) {
+                std::swap(r.p, r.q);  // P_1 = Q_0; the next Q goes where P's array was
+            } else {
+                std::swap(r.p, r.p2);
+            }
+        }
+    }
 
     ApplyArgs aa{};
     aa.recs = table;
     aa.count = count;
     aa.ws = ws;
     aa.scale = scale;
-    aa.final_copy = sp.ns_steps % 2;
-    aa.use_scale = sp.ns_steps == 0 ? 1 : 0;
+    aa.use_scale = steps == 0 ? 1 : 0;
     aa.update = sp.update;
     aa.lr = sp.lr;
     aa.weight_decay = sp.wd;
@@ -219,7 +316,7 @@ extern "C" dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const v
 }
 
 extern "C" int32_t muon_step_event_count(int32_t ns_steps) {
-    return ns_steps < 0 ? -1 : 3 + 3 * ns_steps;
+    return ns_steps < 0 ? -1 : 3 + 4 * ns_steps;
 }
 
 extern "C" dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const void* const* grads,

@@ -17,6 +17,8 @@ constexpr int kPathBF16 = DMUON_BF16;
 // matrix; every tile granularity is a multiple of 64.
 constexpr int kPrepTile = 64;
 constexpr std::size_t kAlign = 256;
+// Gram-space iterations between restarts unless the plan options say otherwise.
+constexpr int32_t kDefaultGramRestart = 3;
 // Longest side a bf16-gradient matrix may have: the bf16 kernels address up
 // to 8 rows of a slab with one 32-bit byte offset per lane.
 constexpr int64_t kMaxBf16Side = int64_t(1) << 27;
@@ -39,6 +41,8 @@ struct MatPlan {
 
 struct BucketPlan {
     int32_t path;          // kPathF32 | kPathBF16
+    int32_t algo;          // DMUON_ALGO_SHORT_SIDE | DMUON_ALGO_GRAM_SPACE
+    int32_t seg_len;       // iterations per segment: 1 (short side) or the Gram-space restart interval
     int32_t tile;          // tile granularity g
     int64_t m_pad, n_pad;
     std::vector<int32_t> members;  // input indices, slot order
@@ -47,8 +51,12 @@ struct BucketPlan {
     int32_t esize;         // bytes per element of X / A / B
     // byte offsets of the bucket's arrays in the workspace; slot s of array Y
     // starts at off_Y + s * (its per-matrix size).  X (m_pad x n_pad) is kept in
-    // two copies that the iterations ping-pong between.
+    // two copies that the iterations ping-pong between.  Gram-space buckets
+    // hold three more m_pad x m_pad arrays (off_g[0..2]); together with A and
+    // B they carry the recurrence's A_k, Q_k, P_k, P_{k+1} and the product
+    // A_k Q_k, whose roles rotate over the iterations.
     std::size_t off_x0, off_x1, off_a, off_b;
+    std::size_t off_g[3];
 };
 
 }  // namespace dmuon
@@ -80,7 +88,7 @@ struct DevMatRec {
     int32_t transposed;
     int32_t src_dtype, dst_dtype, path;
     float upd_scale;       // sqrt(max(1, rows / cols))
-    int32_t pad_;
+    int32_t final_copy;    // X copy (0 | 1) that holds the orthogonalised matrix
 };
 
 // Apply kernel: each block covers kApplyElems elements of the real matrix.

@@ -173,7 +173,7 @@ __device__ __forceinline__ void apply_tile(const ApplyArgs& a, const DevMatRec& 
     const int64_t rho0 = (local / tiles_c) * kPrepTile;
     const int64_t kap0 = (local % tiles_c) * kPrepTile;
     const int t = threadIdx.x, cg = t & 15, rr = t >> 4;
-    const FT* F = reinterpret_cast<const FT*>(a.ws + (a.final_copy ? r.x_off1 : r.x_off0));
+    const FT* F = reinterpret_cast<const FT*>(a.ws + (r.final_copy ? r.x_off1 : r.x_off0));
     DT* W = static_cast<DT*>(r.dst);
     const float sigma = a.use_scale ? a.scale[plan_idx] : 1.0f;
     const float coef = -a.lr * r.upd_scale * sigma;

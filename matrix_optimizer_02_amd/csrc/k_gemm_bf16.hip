@@ -1,13 +1,16 @@
-// The three Newton-Schulz products on bf16 MFMA (gfx950), one grouped launch
-// per phase over every bucket of the batch:
+// The Newton-Schulz products on bf16 MFMA (gfx950), one grouped launch per
+// phase over every bucket of the batch:
 //   Gram    A  = s X X^T           upper-triangle tiles only, mirrored store
 //   square  B' = a I + b A + c A A^T   (A A = A A^T: A is symmetric) upper tiles only
 //   BX      X' = s B' X            into the other X copy
+//   prod    C  = P Q               P, Q symmetric and commuting (the Gram-space
+//                                  recurrence's products), upper tiles only
 // X' = a X + B X is computed as (a I + B) X: the a X term rides on B's
 // diagonal, so the B X epilogue never reads X back.
 // s is 1 / (||U||_F + eps) in the first iteration (s^2 for the Gram) and 1
 // afterwards.  Each product is computed as C[i][j] = sum_k P[i][k] Q[j][k]:
-// for the Gram and square P = Q = X or A, whose rows are K-contiguous; for B X
+// for the Gram and square P = Q = X or A, whose rows are K-contiguous (for the
+// prod two distinct symmetric m x m matrices, rows again K-contiguous); for B X
 // the output tile is X'^T (rows along the long side n, columns along the short
 // side m), P[j][k] = X[k][j] is fetched from the K-major X slab with the gfx950
 // transposing LDS read, and Q = B.
@@ -32,7 +35,7 @@
 #include "tile_map.h"
 
 // which phases deal each XCD a contiguous run of a segment's tiles (bit per
-// phase: 1 Gram, 2 square, 4 B X); 0 keeps the hardware's round-robin
+// phase: 1 Gram, 2 square, 4 B X, 8 prod); 0 keeps the hardware's round-robin
 #ifndef DMUON_XCD_REMAP
 #define DMUON_XCD_REMAP 4
 #endif
@@ -161,8 +164,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
             I = t / sg.tm;
             J = t - I * sg.tm;
         }
-        P = reinterpret_cast<const uint16_t*>(args.ws + sg.x_src_off + slot * sg.x_stride);  // X: m x n
-        Q = reinterpret_cast<const uint16_t*>(args.ws + sg.b_off + slot * sg.a_stride);
+        P = reinterpret_cast<const uint16_t*>(args.ws + sg.p_off + slot * sg.x_stride);  // X: m x n
+        Q = reinterpret_cast<const uint16_t*>(args.ws + sg.q_off + slot * sg.a_stride);
         ldq = sg.m_pad;
     } else {
         if (DMUON_BANDED) {
@@ -176,8 +179,9 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
             I = i;
             J = i + tt;
         }
-        const int64_t off = PHASE == kGram ? sg.x_src_off + slot * sg.x_stride : sg.a_off + slot * sg.a_stride;
-        P = Q = reinterpret_cast<const uint16_t*>(args.ws + off);
+        P = reinterpret_cast<const uint16_t*>(args.ws + sg.p_off +
+                                              slot * (PHASE == kGram ? sg.x_stride : sg.a_stride));
+        Q = PHASE == kProd ? reinterpret_cast<const uint16_t*>(args.ws + sg.q_off + slot * sg.a_stride) : P;
         ldq = PHASE == kGram ? sg.n_pad : sg.m_pad;
     }
     const int64_t K = ldq;
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     // i.e. four consecutive rows r0 .. r0 + 3 of one column c per (i, j, v / 4).
     // The tile goes through LDS transposed, as E[c][r] = C[r][c]: each lane's
     // four values are one 8-byte piece of a row of E.
-    const float first_scale = args.first_iter ? args.scale[plan_idx] : 1.0f;
+    const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
     // T rows of 2 T bytes from global (row stride ld elements) into E, whole.
     auto load_tile = [&](const uint16_t* src, int64_t ld) {
         constexpr int kLoads = T * C::kERowBytes / 1024 / 4;  // 1 KB loads per wave
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         // Tile rows are long-side indices r, columns short-side indices c:
         // X'[c][r] = s acc[r][c]; E is the X' tile (T rows c, T columns r).
         const int64_t ldn = sg.n_pad;
-        uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.x_dst_off + slot * sg.x_stride) +
+        uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + slot * sg.x_stride) +
                        (int64_t)J * T * ldn + (int64_t)I * T;
         #pragma unroll
         for (int i = 0; i < C::F; ++i)
@@ -476,9 +480,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         // The square's b A term reads A's block (J, I) = block (I, J)^T into E
         // first (A is symmetric and stored whole).
         const int64_t ld = sg.m_pad;
-        const int64_t out_off = PHASE == kGram ? sg.a_off + slot * sg.a_stride : sg.b_off + slot * sg.a_stride;
-        uint16_t* Out = reinterpret_cast<uint16_t*>(args.ws + out_off);
-        const float alpha = PHASE == kGram ? first_scale * first_scale : args.c;
+        uint16_t* Out = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + slot * sg.a_stride);
+        const float alpha = PHASE == kGram ? first_scale * first_scale : PHASE == kSquare ? args.c : 1.0f;
         const float beta = args.b;
         if (PHASE == kSquare) load_tile(P + (int64_t)J * T * ld + (int64_t)I * T, ld);
         #pragma unroll
@@ -522,7 +525,9 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
     switch (a.phase) {
         case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram>), grid, block, 0, stream, a); break;
         case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX>), grid, block, 0, stream, a); break;
+        case kBX: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX>), grid, block, 0, stream, a); break;
+        case kProd: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kProd>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

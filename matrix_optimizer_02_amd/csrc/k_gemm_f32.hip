@@ -49,14 +49,13 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
     if (PHASE == kBX) {
         I = t / sg.tm;  // long-side tile
         J = t - I * sg.tm;
-        P = reinterpret_cast<const float*>(args.ws + sg.x_src_off + slot * sg.x_stride);  // X: m x n
-        Q = reinterpret_cast<const float*>(args.ws + sg.b_off + slot * sg.a_stride);
+        P = reinterpret_cast<const float*>(args.ws + sg.p_off + slot * sg.x_stride);  // X: m x n
+        Q = reinterpret_cast<const float*>(args.ws + sg.q_off + slot * sg.a_stride);
         ldk = sg.m_pad;
         K = sg.m_pad;
     } else {
         tri_decode_f(t, sg.tm, I, J);
-        const int64_t off = PHASE == kGram ? sg.x_src_off + slot * sg.x_stride : sg.a_off + slot * sg.a_stride;
-        P = Q = reinterpret_cast<const float*>(args.ws + off);
+        P = Q = reinterpret_cast<const float*>(args.ws + sg.p_off + slot * (PHASE == kGram ? sg.x_stride : sg.a_stride));
         ldk = PHASE == kGram ? sg.n_pad : sg.m_pad;
         K = ldk;
     }
@@ -93,14 +92,14 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
     }
 
     // thread owns rows ty*4 + i and columns tx*4 + j of the 64 x 64 tile
-    const float first_scale = args.first_iter ? args.scale[plan_idx] : 1.0f;
+    const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
     const int64_t r0 = (int64_t)I * kT + ty * 4, c0 = (int64_t)J * kT + tx * 4;
     if (PHASE == kBX) {
         // rows r of the tile are long-side indices, columns c short-side ones:
         // X'[c][r] = s (a X[c][r] + acc[r][c])
         const int64_t ldn = sg.n_pad;
         const float* Xs = P;
-        float* Xd = reinterpret_cast<float*>(args.ws + sg.x_dst_off + slot * sg.x_stride);
+        float* Xd = reinterpret_cast<float*>(args.ws + sg.o_off + slot * sg.x_stride);
         #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float4 xs = *reinterpret_cast<const float4*>(Xs + (c0 + j) * ldn + r0);
@@ -112,8 +111,7 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
         }
     } else {
         const int64_t ld = sg.m_pad;
-        const int64_t out_off = PHASE == kGram ? sg.a_off + slot * sg.a_stride : sg.b_off + slot * sg.a_stride;
-        float* Out = reinterpret_cast<float*>(args.ws + out_off);
+        float* Out = reinterpret_cast<float*>(args.ws + sg.o_off + slot * sg.a_stride);
         const float alpha = PHASE == kGram ? first_scale * first_scale : args.c;
         float o[4][4];
         #pragma unroll
@@ -145,7 +143,8 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream) {
     switch (a.phase) {
         case kGram: hipLaunchKernelGGL(ns_gemm_f32_kernel<kGram>, grid, block, 0, stream, a); break;
         case kSquare: hipLaunchKernelGGL(ns_gemm_f32_kernel<kSquare>, grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL(ns_gemm_f32_kernel<kBX>, grid, block, 0, stream, a); break;
+        case kBX: hipLaunchKernelGGL(ns_gemm_f32_kernel<kBX>, grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;  // fp32 buckets run the short-side recurrence only
     }
     return hipGetLastError();
 }

@@ -40,7 +40,6 @@ struct ApplyArgs {
     int32_t count;
     const char* ws;
     const float* scale;
-    int32_t final_copy;    // which X copy holds the result (ns_steps % 2)
     int32_t use_scale;     // ns_steps == 0: multiply by 1 / (||U|| + eps)
     int32_t update;        // 1: W' = W (1 - lr wd) - lr s O ; 0: dst = O
     float lr;
@@ -51,10 +50,20 @@ hipError_t launch_apply(const ApplyArgs& a, hipStream_t stream);
 
 // ---- Newton-Schulz products (k_gemm_bf16.hip, k_gemm_f32.hip) ---------------
 
-enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
+// Products of one grouped launch, C[i][j] = sum_k P[i][k] Q[j][k]:
+//   kGram    P = Q = X (m_pad x n_pad)       O = s^2 C          triangle, mirrored
+//   kSquare  P = Q = A                       O = a I + b A + c C  triangle, mirrored
+//   kBX      P = X^T (read from X), Q = B'   O = s C^T  (m_pad x n_pad)
+//   kProd    P, Q two symmetric m x m        O = C              triangle, mirrored
+// kProd serves the Gram-space recurrence, whose operands all commute, so the
+// product of two of them is symmetric.
+enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2, kProd = 3 };
 constexpr int kMaxSeg = 24;
 
-// One bucket's share of a grouped launch.
+// One bucket's share of a grouped launch.  Operand and output arrays are given
+// as bucket base byte offsets in the workspace; slot s adds s times the
+// per-slot size: x_stride for m_pad x n_pad arrays (the Gram's P and Q, the
+// B X product's P and O), a_stride for m_pad x m_pad ones.
 struct GemmSeg {
     int32_t first_block;    // first block id of this segment in the launch
     int32_t tiles_per_mat;  // output tiles per matrix
@@ -62,9 +71,11 @@ struct GemmSeg {
     int32_t tn;             // tiles along the long side (n_pad / tile)
     int32_t count;          // matrices in the bucket
     int32_t plan_base;      // plan index of slot 0
+    int32_t first_iter;     // apply the normalisation scale s (Gram s^2, B X s)
+    int32_t pad_;
     int64_t m_pad, n_pad;
-    int64_t x_src_off, x_dst_off, a_off, b_off;  // bucket base byte offsets (X read / written)
-    int64_t x_stride, a_stride;                           // per-slot bytes
+    int64_t p_off, q_off, o_off;  // operand P, operand Q (kProd, kBX), output
+    int64_t x_stride, a_stride;   // per-slot bytes
 };
 
 struct GemmArgs {
@@ -72,7 +83,6 @@ struct GemmArgs {
     const float* scale;  // per plan index: 1 / (||U|| + eps)
     float a, b, c;
     int32_t phase;
-    int32_t first_iter;  // apply the normalisation scale in this iteration's epilogues
     int32_t nseg;
     int32_t total_blocks;
     GemmSeg seg[kMaxSeg];

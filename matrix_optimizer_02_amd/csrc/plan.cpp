@@ -9,6 +9,13 @@
 // speed-up); work is balanced by computational cost (DMuon abstract).  The
 // cost of one iteration on an m x n matrix (m <= n) is taken as
 // 4 m^2 n + 2 m^3: the products X X^T, A A and B X.
+//
+// Each bf16 bucket whose padded long side exceeds its padded short side runs,
+// by default, the Gram-space form of the recurrence (DMuon explainer on
+// gist.science, second section 2.1 Efficiente Gram Newton-Schulz Iteratie):
+// most of its products are m x m; with the default restart every 3
+// iterations, 5 iterations cost 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3.
+// The bucket ordering keeps the cost above.
 #include <algorithm>
 #include <map>
 #include <new>
@@ -33,9 +40,15 @@ bool valid_dtype(int32_t d) { return d == DMUON_F32 || d == DMUON_BF16; }
 
 }  // namespace
 
-extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out) {
+extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t count, const dmuon_plan_opts* opts,
+                                     dmuon_plan** out) {
     if (out == nullptr || count < 0 || (count > 0 && descs == nullptr)) return DMUON_ERR_INVALID_ARG;
     *out = nullptr;
+    const int32_t algo_opt = opts ? opts->algo : DMUON_ALGO_AUTO;
+    if (algo_opt != DMUON_ALGO_AUTO && algo_opt != DMUON_ALGO_SHORT_SIDE && algo_opt != DMUON_ALGO_GRAM_SPACE)
+        return DMUON_ERR_INVALID_ARG;
+    if (opts && opts->gram_restart < 0) return DMUON_ERR_INVALID_ARG;
+    const int32_t restart = opts && opts->gram_restart > 0 ? opts->gram_restart : kDefaultGramRestart;
     for (int32_t i = 0; i < count; ++i) {
         const dmuon_matrix_desc& d = descs[i];
         if (d.rows < 1 || d.cols < 1 || !valid_dtype(d.grad_dtype) || !valid_dtype(d.param_dtype))
@@ -87,6 +100,21 @@ extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count,
             }
             tmp[b].members.push_back(i);
         }
+        // Recurrence form.  The Gram space does less work once the padded long
+        // side exceeds the padded short one; by default it is also kept off
+        // buckets holding a matrix whose real long side is under 1.5 times its
+        // short side (a near-square matrix has small singular values, which the
+        // Gram space resolves worse, and there it saves little).  fp32 buckets
+        // keep the short side.
+        for (auto& bp : tmp) {
+            bool gram = bp.path == kPathBF16 && algo_opt != DMUON_ALGO_SHORT_SIDE;
+            if (gram && algo_opt == DMUON_ALGO_AUTO) {
+                gram = bp.n_pad > bp.m_pad;
+                for (int32_t i : bp.members) gram = gram && 2 * p->mats[i].n >= 3 * p->mats[i].m;
+            }
+            bp.algo = gram ? DMUON_ALGO_GRAM_SPACE : DMUON_ALGO_SHORT_SIDE;
+            bp.seg_len = gram ? restart : 1;
+        }
         // order buckets by executed cost, descending; stable sort keeps first appearance on ties
         for (auto& bp : tmp) bp.exec_cost = (int64_t)bp.members.size() * dense_cost(bp.m_pad, bp.n_pad);
         std::vector<int32_t> idx(tmp.size());
@@ -133,6 +161,10 @@ extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count,
             bp.off_x1 = off;  off = align_up(off + cnt * xsz);
             bp.off_a = off;   off = align_up(off + cnt * asz);
             bp.off_b = off;   off = align_up(off + cnt * asz);
+            for (int g = 0; g < 3; ++g) {
+                bp.off_g[g] = off;
+                if (bp.algo == DMUON_ALGO_GRAM_SPACE) off = align_up(off + cnt * asz);
+            }
         }
         p->workspace_bytes = count == 0 ? 0 : off;
     } catch (const std::bad_alloc&) {
@@ -141,6 +173,10 @@ extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count,
     }
     *out = p;
     return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out) {
+    return muon_plan_ex(descs, count, nullptr, out);
 }
 
 extern "C" dmuon_status muon_plan_workspace_bytes(const dmuon_plan* plan, size_t* bytes) {
@@ -181,6 +217,14 @@ extern "C" dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket,
     if (padded_n) *padded_n = bp.n_pad;
     if (count) *count = (int32_t)bp.members.size();
     if (tile) *tile = bp.tile;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bucket, int32_t* algo,
+                                             int32_t* gram_restart) {
+    if (plan == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size()) return DMUON_ERR_INVALID_ARG;
+    if (algo) *algo = plan->buckets[bucket].algo;
+    if (gram_restart) *gram_restart = plan->buckets[bucket].seg_len;
     return DMUON_OK;
 }
 

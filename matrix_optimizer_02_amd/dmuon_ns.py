@@ -56,6 +56,15 @@ class AdamWHParams(ctypes.Structure):
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
 
 
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("gram_restart", ctypes.c_int32)]
+
+
+# dmuon_algo
+ALGO_AUTO, ALGO_SHORT_SIDE, ALGO_GRAM_SPACE = 0, 1, 2
+_ALGO_CODE = {"auto": ALGO_AUTO, "short_side": ALGO_SHORT_SIDE, "gram_space": ALGO_GRAM_SPACE}
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built: run `python -m matrix_optimizer_02_amd.build`")
@@ -65,6 +74,8 @@ def _load():
     vpp = ctypes.POINTER(ctypes.c_void_p)
     sig = {
         "muon_plan": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, vpp]),
+        "muon_plan_ex": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts), vpp]),
+        "muon_plan_bucket_algo": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p]),
         "muon_plan_workspace_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
         "muon_plan_info": (ctypes.c_int, [ctypes.c_void_p, c_int32_p, c_int32_p]),
         "muon_plan_query": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p,
@@ -135,21 +146,26 @@ class BucketEntry:
     padded_n: int
     count: int
     tile: int
+    algo: int          # ALGO_SHORT_SIDE | ALGO_GRAM_SPACE
+    gram_restart: int  # iterations per Gram-space segment (1 on the short side)
 
 
 class Plan:
     """Owner of a dmuon_plan (host memory only)."""
 
-    def __init__(self, descs: Sequence[tuple]):
+    def __init__(self, descs: Sequence[tuple], algo="auto", gram_restart: int = 0):
         """descs: (rows, cols, grad_dtype, param_dtype); dtypes as torch dtypes,
-        "bf16"/"f32" or the DMUON_* codes."""
+        "bf16"/"f32" or the DMUON_* codes.  algo: "auto", "short_side" or
+        "gram_space" (or the ALGO_* codes); gram_restart: Gram-space
+        iterations between restarts (0: the library's default)."""
         self.descs = [(int(r), int(c), _code(g), _code(p)) for (r, c, g, p) in descs]
         arr = (MatrixDesc * max(1, len(self.descs)))()
         for i, (r, c, g, p) in enumerate(self.descs):
             arr[i] = MatrixDesc(r, c, g, p)
         handle = ctypes.c_void_p()
         self._destroy = _lib.muon_plan_destroy
-        _check(_lib.muon_plan(arr, len(self.descs), ctypes.byref(handle)), "muon_plan")
+        opts = PlanOpts(algo if isinstance(algo, int) else _ALGO_CODE[algo], int(gram_restart))
+        _check(_lib.muon_plan_ex(arr, len(self.descs), ctypes.byref(opts), ctypes.byref(handle)), "muon_plan_ex")
         self._h = handle
 
     @property
@@ -182,7 +198,10 @@ class Plan:
         pm, pn = ctypes.c_int64(), ctypes.c_int64()
         _check(_lib.muon_plan_bucket(self._h, int(b), ctypes.byref(path), ctypes.byref(pm), ctypes.byref(pn),
                                      ctypes.byref(cnt), ctypes.byref(tile)), "muon_plan_bucket")
-        return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value)
+        algo, restart = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.muon_plan_bucket_algo(self._h, int(b), ctypes.byref(algo), ctypes.byref(restart)),
+               "muon_plan_bucket_algo")
+        return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value)
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -199,17 +218,18 @@ def _code(d) -> int:
     return _DTYPE_CODE[d]
 
 
-def muon_plan(descs: Sequence[tuple]) -> Plan:
-    return Plan(descs)
+def muon_plan(descs: Sequence[tuple], algo="auto", gram_restart: int = 0) -> Plan:
+    return Plan(descs, algo, gram_restart)
 
 
-def plan_for(tensors_or_shapes: Sequence, param_dtypes: Optional[Sequence] = None) -> Plan:
+def plan_for(tensors_or_shapes: Sequence, param_dtypes: Optional[Sequence] = None, algo="auto",
+             gram_restart: int = 0) -> Plan:
     """Plan from gradient tensors (shape and dtype) and parameter dtypes."""
     descs = []
     for i, g in enumerate(tensors_or_shapes):
         pd = g.dtype if param_dtypes is None else param_dtypes[i]
         descs.append((g.shape[0], g.shape[1], g.dtype, pd))
-    return Plan(descs)
+    return Plan(descs, algo, gram_restart)
 
 
 def workspace_for(plan: Plan, device=None) -> torch.Tensor:
@@ -318,7 +338,7 @@ def adamw_step_batched(params: Sequence[torch.Tensor], grads: Sequence[torch.Ten
 class PhaseEvents:
     """HIP events for muon_step_batched_profiled: one set per step to time."""
 
-    PHASES_PER_ITER = ("gram", "square", "bx")
+    PHASES_PER_ITER = ("gram", "square", "prod", "bx")
 
     def __init__(self, ns_steps: int):
         self.ns_steps = int(ns_steps)
@@ -377,8 +397,9 @@ def muon_step_batched_profiled(plan: Plan, grads, momenta, params, events: Phase
 class MuonBatch:
     """Convenience owner of a plan and its workspace for a fixed matrix set."""
 
-    def __init__(self, grads: Sequence[torch.Tensor], params: Sequence[torch.Tensor]):
-        self.plan = plan_for(grads, [p.dtype for p in params])
+    def __init__(self, grads: Sequence[torch.Tensor], params: Sequence[torch.Tensor], algo="auto",
+                 gram_restart: int = 0):
+        self.plan = plan_for(grads, [p.dtype for p in params], algo, gram_restart)
         self.workspace = workspace_for(self.plan, grads[0].device if len(grads) else None)
 
     def step(self, grads, momenta, params, **hp):
@@ -391,4 +412,5 @@ class MuonBatch:
 __all__ = ["Plan", "PlanEntry", "BucketEntry", "MuonBatch", "DMuonError", "PhaseEvents", "muon_plan",
            "plan_for", "workspace_for", "muon_step_batched", "muon_step_batched_profiled",
            "ns_orthogonalize_batched", "status_string",
-           "version", "library_path", "DMUON_F32", "DMUON_BF16"]
+           "version", "library_path", "DMUON_F32", "DMUON_BF16", "ALGO_AUTO", "ALGO_SHORT_SIDE",
+           "ALGO_GRAM_SPACE", "PlanOpts"]

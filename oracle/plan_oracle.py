@@ -19,10 +19,20 @@ documented contract for that step, written out plainly:
   4 m_pad^2 n_pad + 2 m_pad^3, descending; ties keep the order in which the
   bucket key first appears;
 * inside a bucket, members keep their input order (slot 0, 1, ...);
-* the reported per-matrix cost is 4 m^2 n + 2 m^3 of the real shape.
+* the reported per-matrix cost is 4 m^2 n + 2 m^3 of the real shape;
+* recurrence form per bucket: the Gram-space form (the iteration carried in
+  the m x m Gram space, DMuon explainer on gist.science, second section 2.1
+  Efficiente Gram Newton-Schulz Iteratie) on the bf16 path when n_pad > m_pad
+  and every member has n >= 1.5 m under the default option, on every bf16
+  bucket when it is forced; the
+  short-side form otherwise, and always on the f32 path.  A Gram-space bucket
+  restarts every ``gram_restart`` iterations (default 3); a short-side bucket
+  reports 1.
 """
 
 from __future__ import annotations
+
+DEFAULT_GRAM_RESTART = 3
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -42,11 +52,25 @@ def _cost(m: int, n: int) -> int:
     return 4 * m * m * n + 2 * m * m * m
 
 
-def plan_reference(descs):
+def bucket_algo(path: str, m_pad: int, n_pad: int, shapes, option: str = "auto") -> str:
+    """"gram_space" or "short_side" for a bucket whose members have the real
+    (m, n) in ``shapes``; option is "auto", "short_side" or "gram_space"."""
+    if path != "bf16" or option == "short_side":
+        return "short_side"
+    if option == "gram_space":
+        return "gram_space"
+    if n_pad > m_pad and all(n >= 1.5 * m for m, n in shapes):
+        return "gram_space"
+    return "short_side"
+
+
+def plan_reference(descs, algo: str = "auto", gram_restart: int = 0):
     """descs: list of (rows, cols, grad_dtype, param_dtype) with dtype codes
     0 = fp32, 1 = bf16.  Returns a list of per-matrix dicts with keys
     bucket, slot, transposed, m, n, m_pad, n_pad, cost, and the list of
-    buckets (path, m_pad, n_pad, members) in execution order."""
+    buckets (path, m_pad, n_pad, members, algo, gram_restart) in execution
+    order."""
+    restart = gram_restart if gram_restart > 0 else DEFAULT_GRAM_RESTART
     items = []
     keys_in_order = []
     members = {}
@@ -72,6 +96,7 @@ def plan_reference(descs):
         for slot, idx in enumerate(members[key]):
             items[idx]["bucket"] = b
             items[idx]["slot"] = slot
-        buckets.append({"path": key[0], "m_pad": key[1], "n_pad": key[2],
-                        "members": list(members[key])})
+        form = bucket_algo(key[0], key[1], key[2], [(items[i]["m"], items[i]["n"]) for i in members[key]], algo)
+        buckets.append({"path": key[0], "m_pad": key[1], "n_pad": key[2], "members": list(members[key]),
+                        "algo": form, "gram_restart": restart if form == "gram_space" else 1})
     return items, buckets

@@ -23,8 +23,9 @@ host_only = pytest.mark.skipif(torch.cuda.is_available(),
 def test_exports_every_declared_symbol():
     raw = ctypes.CDLL(d.library_path())
     names = build_mod.exported_symbols()
-    assert set(names) == {"muon_plan", "muon_plan_workspace_bytes", "muon_plan_info", "muon_plan_query",
-                          "muon_plan_bucket", "muon_plan_destroy", "muon_step_batched",
+    assert set(names) == {"muon_plan", "muon_plan_ex", "muon_plan_workspace_bytes", "muon_plan_info",
+                          "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_destroy",
+                          "muon_step_batched",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
                           "adamw_step_batched", "dmuon_status_string", "dmuon_version"}
@@ -33,7 +34,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_event_count():
-    assert LIB.muon_step_event_count(5) == 18 and LIB.muon_step_event_count(0) == 3
+    # prep, 4 phases per iteration (Gram, square, prod, B X), apply, and the start event
+    assert LIB.muon_step_event_count(5) == 23 and LIB.muon_step_event_count(0) == 3
+    assert LIB.muon_step_event_count(1) == 7
     assert LIB.muon_step_event_count(-1) == -1
 
 
@@ -56,11 +59,16 @@ CASES = {
 }
 
 
+ALGO = {"short_side": d.ALGO_SHORT_SIDE, "gram_space": d.ALGO_GRAM_SPACE}
+
+
+@pytest.mark.parametrize("algo,restart", [("auto", 0), ("short_side", 0), ("gram_space", 0), ("gram_space", 2),
+                                          ("auto", 5)])
 @pytest.mark.parametrize("name", sorted(WORKLOADS) + sorted(CASES))
-def test_plan_matches_reference(name):
+def test_plan_matches_reference(name, algo, restart):
     descs = CASES[name] if name in CASES else _descs_of(WORKLOADS[name])
-    items, buckets = plan_reference(descs)
-    p = d.Plan(descs)
+    items, buckets = plan_reference(descs, algo, restart)
+    p = d.Plan(descs, algo, restart)
     assert p.info() == (len(descs), len(buckets))
     for i, it in enumerate(items):
         e = p.query(i)
@@ -71,6 +79,23 @@ def test_plan_matches_reference(name):
         assert (e.path, e.padded_m, e.padded_n, e.count) == (
             0 if bk["path"] == "f32" else 1, bk["m_pad"], bk["n_pad"], len(bk["members"]))
         assert e.tile == (64 if bk["path"] == "f32" else (128 if bk["m_pad"] <= 128 else 256))
+        assert (e.algo, e.gram_restart) == (ALGO[bk["algo"]], bk["gram_restart"]), b
+
+
+def test_default_algo_by_hand():
+    # bf16: Gram space exactly when the padded long side exceeds the padded short side
+    # whose members all have n >= 1.5 m
+    p = d.Plan([(4096, 14336, 1, 1), (4096, 4096, 1, 1), (1024, 4096, 0, 0), (200, 256, 1, 1),
+                (128, 192, 1, 1), (100, 250, 1, 1), (384, 1000, 1, 1), (300, 1000, 1, 1)])
+    got = {(p.bucket(b).padded_m, p.bucket(b).padded_n, p.bucket(b).path): p.bucket(b).algo
+           for b in range(p.info()[1])}
+    assert got == {(4096, 14336, 1): d.ALGO_GRAM_SPACE, (4096, 4096, 1): d.ALGO_SHORT_SIDE,
+                   (1024, 4096, 0): d.ALGO_SHORT_SIDE, (256, 256, 1): d.ALGO_SHORT_SIDE,
+                   (128, 256, 1): d.ALGO_GRAM_SPACE, (512, 1024, 1): d.ALGO_GRAM_SPACE}
+    # one near-square member keeps its whole bucket on the short side
+    p = d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)])
+    assert p.info()[1] == 1 and p.bucket(0).algo == d.ALGO_SHORT_SIDE
+    assert d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)], "gram_space").bucket(0).algo == d.ALGO_GRAM_SPACE
 
 
 def test_workspace_covers_operands():
@@ -81,7 +106,12 @@ def test_workspace_covers_operands():
         es = 2 if bk["path"] == "bf16" else 4
         cnt = len(bk["members"])
         need += cnt * es * (2 * bk["m_pad"] * bk["n_pad"] + 2 * bk["m_pad"] ** 2)
+        if bk["algo"] == "gram_space":  # P_k, P_{k+1} and A_k Q_k
+            need += cnt * es * 3 * bk["m_pad"] ** 2
     assert d.Plan(descs).workspace_bytes() >= need
+    # forcing the short side needs no Gram-space arrays, forcing the Gram space more
+    assert d.Plan(descs, "short_side").workspace_bytes() < d.Plan(descs).workspace_bytes()
+    assert d.Plan(descs, "gram_space").workspace_bytes() > d.Plan(descs).workspace_bytes()
     assert d.Plan([]).workspace_bytes() == 0
 
 
@@ -104,7 +134,16 @@ def test_plan_errors():
     out = ctypes.c_void_p()
     assert LIB.muon_plan(None, 3, ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
     assert LIB.muon_plan(None, -1, ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
+    arr = (d.MatrixDesc * 1)(d.MatrixDesc(8, 8, 1, 1))
+    assert LIB.muon_plan_ex(arr, 1, ctypes.byref(d.PlanOpts(3, 0)), ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_ex(arr, 1, ctypes.byref(d.PlanOpts(0, -1)), ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_ex(arr, 1, None, ctypes.byref(out)) == d.DMUON_OK
+    LIB.muon_plan_destroy(out)
+    algo = ctypes.c_int32()
+    assert LIB.muon_plan_bucket_algo(None, 0, ctypes.byref(algo), None) == d.DMUON_ERR_INVALID_ARG
     p = d.Plan([(8, 8, 1, 1)])
+    assert LIB.muon_plan_bucket_algo(p.handle, 1, ctypes.byref(algo), None) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_bucket_algo(p.handle, 0, None, None) == d.DMUON_OK
     with pytest.raises(d.DMuonError):
         p.query(1)
     with pytest.raises(d.DMuonError):

@@ -58,14 +58,14 @@ def check_param(Wn_gpu, W0, out_ref, dtype, path, rows, cols):
     assert err <= bound, (err, bound)
 
 
-def step_gpu(w, seed=0, param_dtype=None, zero_params=False, ns_steps=5, steps=1):
+def step_gpu(w, seed=0, param_dtype=None, zero_params=False, ns_steps=5, steps=1, algo="auto", restart=0):
     """Run ``steps`` fused steps on a workload; returns host inputs and outputs."""
     G, M, W = make_inputs(w, "cuda", seed)
     if param_dtype is not None or zero_params:
         pd = param_dtype or torch.float32
         W = [torch.zeros_like(x, dtype=pd) if zero_params else x.to(pd) for x in W]
     host = {"G": [f64(x) for x in G], "M": [f64(x) for x in M], "W": [f64(x) for x in W]}
-    plan = d.plan_for(G, [x.dtype for x in W])
+    plan = d.plan_for(G, [x.dtype for x in W], algo, restart)
     ws = d.workspace_for(plan)
     for _ in range(steps):
         d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=ns_steps, workspace=ws)
@@ -73,8 +73,8 @@ def step_gpu(w, seed=0, param_dtype=None, zero_params=False, ns_steps=5, steps=1
     return host, {"M": [f64(x) for x in M], "W": [f64(x) for x in W]}, G, M, W
 
 
-def orth_gpu(inputs, out_dtype=torch.float32, ns_steps=5, eps=EPS):
-    plan = d.plan_for(inputs, [out_dtype] * len(inputs))
+def orth_gpu(inputs, out_dtype=torch.float32, ns_steps=5, eps=EPS, algo="auto", restart=0):
+    plan = d.plan_for(inputs, [out_dtype] * len(inputs), algo, restart)
     ws = d.workspace_for(plan)
     outs = [torch.empty(x.shape, dtype=out_dtype, device="cuda") for x in inputs]
     d.ns_orthogonalize_batched(plan, inputs, outs, ns_steps=ns_steps, eps=eps, workspace=ws)
@@ -118,11 +118,12 @@ def test_small_batch_step_bf16_params():
         check_param(out["W"][i], host["W"][i], ref, "bf16", "bf16", spec.rows, spec.cols)
 
 
-def test_small_batch_step_recovers_O():
+@pytest.mark.parametrize("algo", ["auto", "short_side"])
+def test_small_batch_step_recovers_O(algo):
     # W = 0 in fp32: W' = -lr s O exposes the step's own orthogonalised update
     w = get_workload("bf16_small_batch_96")
-    say("case bf16_small_batch_96 muon_step_batched fp32 zero params")
-    host, out, *_ = step_gpu(w, zero_params=True)
+    say(f"case bf16_small_batch_96 muon_step_batched fp32 zero params, {algo}")
+    host, out, *_ = step_gpu(w, zero_params=True, algo=algo)
     errs = []
     for i, spec in enumerate(w.matrices):
         ref = oracle.muon_step(host["G"][i], host["M"][i], host["W"][i], lr=LR, beta=BETA, eps=EPS)
@@ -142,14 +143,16 @@ SHAPE_SETS = {
 }
 
 
+# the default (Gram space on the buckets with padded n > padded m) and the short side forced
+@pytest.mark.parametrize("algo", ["auto", "short_side"])
 @pytest.mark.parametrize("name", sorted(SHAPE_SETS))
-@pytest.mark.parametrize("ns_steps", [0, 1, 5])
-def test_orthogonalize_shapes(name, ns_steps):
+@pytest.mark.parametrize("ns_steps", [0, 1, 2, 5])
+def test_orthogonalize_shapes(name, ns_steps, algo):
     shapes, dt = SHAPE_SETS[name]
     w = custom_workload(name, shapes, dt, dt, g_std=1.0)
     Gs = [host_tensor(w, i, GRAD, seed=3) for i in range(w.count)]
-    say(f"case {name} ns_orthogonalize_batched ns_steps={ns_steps}")
-    outs = orth_gpu([g.cuda() for g in Gs], ns_steps=ns_steps)
+    say(f"case {name} ns_orthogonalize_batched ns_steps={ns_steps} {algo}")
+    outs = orth_gpu([g.cuda() for g in Gs], ns_steps=ns_steps, algo=algo)
     for i, g in enumerate(Gs):
         ref = oracle.newton_schulz(f64(g), ns_steps, A, B, C, EPS)
         assert rel(f64(outs[i]), ref) < TOL[dt], (shapes[i], rel(f64(outs[i]), ref))
@@ -233,6 +236,71 @@ def test_rank_one_and_diagonal_inputs():
         e = rel(f64(o), oracle.newton_schulz(f64(xin), 5, A, B, C, EPS))
         say(f"  rel err {e:.3e} (tol {tol:.1e})")
         assert e < tol
+
+
+# ---- the Gram-space recurrence: restart intervals, conditioning, growth bound ---------
+
+GRAM_SHAPES = [(256, 768), (768, 256), (384, 1000), (128, 640), (72, 200), (512, 1536)]
+
+
+@pytest.mark.parametrize("restart", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("ns_steps", [1, 2, 3, 4, 5])
+def test_gram_space_restart_intervals(restart, ns_steps):
+    # every segmentation of up to 5 iterations (the last segment shorter, a
+    # single segment, one-iteration segments) against the oracle, on Gaussian
+    # inputs
+    w = custom_workload("gram", GRAM_SHAPES, "bf16", "bf16", g_std=1.0)
+    Gs = [host_tensor(w, i, GRAD, seed=7) for i in range(w.count)]
+    say(f"case Gram space restart {restart} ns_steps {ns_steps}")
+    outs = orth_gpu([g.cuda() for g in Gs], ns_steps=ns_steps, algo="gram_space", restart=restart)
+    for i, g in enumerate(Gs):
+        e = rel(f64(outs[i]), oracle.newton_schulz(f64(g), ns_steps, A, B, C, EPS))
+        assert e < TOL["bf16"], (GRAM_SHAPES[i], e)
+
+
+def _spectrum_input(m, n, sv, seed):
+    r = np.random.default_rng(seed)
+    u, _ = np.linalg.qr(r.standard_normal((m, m)))
+    v, _ = np.linalg.qr(r.standard_normal((n, m)))
+    return torch.from_numpy(((u * sv) @ v.T).astype(np.float32)).to(torch.bfloat16)
+
+
+def test_gram_space_ill_conditioned_inputs():
+    # Singular values 1 / (1 + i) and exp(-8 i / m): the Gram space squares the
+    # condition number, so in bf16 it resolves small singular values far worse
+    # than the short side; restarting every 3 iterations keeps its error within
+    # 2x of the short side's (which itself exceeds the Gaussian-input bound on
+    # such inputs), while a single 5-iteration segment is several times worse.
+    m, n = 512, 1792
+    cases = {"power": 1.0 / (1.0 + np.arange(m)), "exp": np.exp(-8.0 * np.arange(m) / m)}
+    for name, sv in cases.items():
+        x = _spectrum_input(m, n, sv, seed=12)
+        ref = oracle.newton_schulz(f64(x), 5, A, B, C, EPS)
+        err = {}
+        for algo, restart in (("short_side", 0), ("gram_space", 3), ("gram_space", 5)):
+            o = orth_gpu([x.cuda()], algo=algo, restart=restart)[0]
+            err[(algo, restart)] = rel(f64(o), ref)
+        say(f"case ill-conditioned {name} {m}x{n}: " + ", ".join(f"{k} {v:.3e}" for k, v in err.items()))
+        short, gram3, gram5 = err[("short_side", 0)], err[("gram_space", 3)], err[("gram_space", 5)]
+        assert gram3 < 2 * short
+        assert gram5 > 3 * gram3
+
+
+def test_gram_space_growth_bound_falls_back():
+    # Beyond |a|^gram_restart = 2^64 a call runs Gram-space buckets on the short
+    # side: the same products as a short-side plan, so the same bits.  Below it
+    # the two forms differ (rounding), which shows the Gram space ran.
+    w = custom_workload("fallback", [(256, 768), (384, 128)], "bf16", "bf16", g_std=1.0)
+    Gs = [host_tensor(w, i, GRAD, seed=6).cuda() for i in range(w.count)]
+    bits = lambda t: t.view(torch.int32)
+    over = math.floor(64 / math.log2(A)) + 1
+    say(f"case Gram-space growth bound, restart {over}, ns_steps {over}")
+    runs = [orth_gpu(Gs, ns_steps=over, algo="gram_space", restart=over),
+            orth_gpu(Gs, ns_steps=over, algo="short_side")]
+    for x, y in zip(*runs):
+        assert torch.equal(bits(x), bits(y))
+    under = [orth_gpu(Gs, ns_steps=5, algo=al) for al in ("gram_space", "short_side")]
+    assert not torch.equal(under[0][0], under[1][0])
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -326,12 +394,15 @@ def test_full_size_step_sampled(wname):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wname", FULL_SETS)
-def test_full_size_orthogonalize_sampled(wname):
+FULL_ORTH = [(wn, "auto") for wn in FULL_SETS] + [("llama3.1-8b_owner_1of8", "short_side")]
+
+
+@pytest.mark.parametrize("wname,algo", FULL_ORTH)
+def test_full_size_orthogonalize_sampled(wname, algo):
     w = get_workload(wname)
-    say(f"case {wname} full ns_orthogonalize_batched bf16 in, fp32 out")
+    say(f"case {wname} full ns_orthogonalize_batched bf16 in, fp32 out, {algo}")
     G, _, _ = make_inputs(w, "cuda", seed=2)
-    outs = orth_gpu(G)
+    outs = orth_gpu(G, algo=algo)
     for i in _samples(w):
         spec = w.matrices[i]
         say(f"  oracle sample {i} {spec.name} {spec.rows}x{spec.cols}")
