@@ -204,9 +204,11 @@ class Plan:
         return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value)
 
     def close(self):
-        if getattr(self, "_h", None) is not None and self._h.value:
-            self._destroy(self._h)
-            self._h = ctypes.c_void_p()
+        # no module globals here: this also runs from __del__ at interpreter exit
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+        self._h = None
 
     def __del__(self):
         self.close()
@@ -345,8 +347,8 @@ class PhaseEvents:
         self.n = _lib.muon_step_event_count(self.ns_steps)
         self.arr = (ctypes.c_void_p * self.n)()
         self._destroy = _lib.dmuon_events_destroy
-        _check(_lib.dmuon_events_create(self.n, ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p))),
-               "dmuon_events_create")
+        self._arr_p = ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p))
+        _check(_lib.dmuon_events_create(self.n, self._arr_p), "dmuon_events_create")
 
     def names(self) -> List[str]:
         out = ["prep"]
@@ -366,8 +368,8 @@ class PhaseEvents:
 
     def close(self):
         if getattr(self, "arr", None) is not None:
-            self._destroy(self.n, ctypes.cast(self.arr, ctypes.POINTER(ctypes.c_void_p)))
-            self.arr = None
+            self._destroy(self.n, self._arr_p)
+            self.arr = self._arr_p = None
 
     def __del__(self):
         self.close()
