@@ -155,6 +155,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW companion measurement")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tuning-cache", default=None, metavar="PATH",
+                    help="run the plan with per-shape tuning entries: loaded from PATH for this device, "
+                         "or measured with muon_autotune on the benchmark inputs and saved there")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times): the reference "
                          "dispatch for scaling HBM traffic counters")
@@ -206,7 +209,18 @@ def main(argv=None):
             host_samples.append((i, (G[i].double().cpu().numpy(), M[i].double().cpu().numpy(),
                                      W[i].double().cpu().numpy())))
 
-    plan = d.plan_for(G, [x.dtype for x in W])
+    tuning, tuning_info = None, None
+    if args.tuning_cache:
+        tuning = d.load_tuning(args.tuning_cache)
+        source = "loaded"
+        if not tuning:
+            t0 = time.perf_counter()
+            tuning = d.autotune(G, [torch.float32] * len(G), reps=2)
+            source = f"measured ({time.perf_counter() - t0:.1f} s)"
+            d.save_tuning(tuning, args.tuning_cache)
+        tuning_info = {"cache": args.tuning_cache, "device": d.device_key(), "source": source,
+                       "entries": [e.to_dict() for e in tuning]}
+    plan = d.plan_for(G, [x.dtype for x in W], tuning=tuning)
     ws = d.workspace_for(plan, dev)
     stream = torch.cuda.current_stream()
 
@@ -298,6 +312,8 @@ def main(argv=None):
                   "gbps": round(apply_bytes / (avg["apply"] / 1e3) / 1e9, 1),
                   "frac_hbm": round(apply_bytes / (avg["apply"] / 1e3) / HBM_PEAK_BPS, 4)},
     }
+    if tuning_info is not None:
+        out["tuning"] = tuning_info
     if not args.no_adamw:
         out["adamw"] = adamw_bench(d, dev)
     if host_samples:

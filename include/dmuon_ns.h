@@ -114,6 +114,31 @@ typedef enum {
     DMUON_ALGO_GRAM_SPACE = 2
 } dmuon_algo;
 
+/* A per-shape configuration (tuning cache entry): how the plan runs a bucket of
+ * the given path and padded dims (the padded dims the default tile granularity
+ * gives).  The pages autotune kernel configurations per matrix shape and cache
+ * the result, and balance work by measured per-shape cost (DMuon explainer on
+ * gist.science, sections 2.3 and 2.4); muon_autotune measures these entries on
+ * the device, and muon_plan_ex applies them. */
+#define DMUON_XCD_REMAP_DEFAULT 0xFFFFFFFFu
+typedef struct {
+    int32_t path;            /* DMUON_BF16 | DMUON_F32 (key) */
+    int32_t tile;            /* output tile edge: bf16 128 or 256 (dividing both padded dims), fp32 64;
+                                0: the default granularity */
+    int64_t padded_m;        /* key: padded short side */
+    int64_t padded_n;        /* key: padded long side */
+    int32_t algo;            /* dmuon_algo for the bucket; DMUON_ALGO_AUTO: the plan option's rule.
+                                DMUON_ALGO_GRAM_SPACE is accepted on the bf16 path only */
+    int32_t gram_restart;    /* Gram-space iterations between restarts; 0: the plan option's */
+    uint32_t xcd_remap;      /* bf16 path: bit per phase (1 Gram, 2 square, 4 B X, 8 prod) whose launch
+                                gives each XCD a contiguous run of the bucket's tiles (neighbouring tiles
+                                share operand panels in that XCD's L2); DMUON_XCD_REMAP_DEFAULT: B X only */
+    int32_t reserved;        /* 0 */
+    double cost_ms_per_matrix; /* measured time of one matrix's Newton-Schulz iterations; when every
+                                  bucket of a plan has one > 0, buckets are ordered by count times it
+                                  instead of the dense cost */
+} dmuon_tune_entry;
+
 typedef struct {
     int32_t algo;         /* dmuon_algo; DMUON_ALGO_AUTO (the default) picks the Gram space for
                              bf16 buckets with padded n > padded m whose members all have
@@ -124,17 +149,23 @@ typedef struct {
     int32_t gram_restart; /* Gram-space iterations between restarts, >= 1; 0: the default, 3.
                              Larger values save m^2 n work and lose accuracy on
                              ill-conditioned inputs; 1 is the short side. */
+    const dmuon_tune_entry* tuned; /* host array of per-shape entries (NULL: none); for each bucket
+                             the first entry with its key applies, entries matching no bucket are
+                             ignored.  Only read during the call. */
+    int32_t tuned_count;
 } dmuon_plan_opts;
 
 /* Build the batch plan (host only, no device work).  Per matrix: m = min(rows,
  * cols), n = max(rows, cols), transposed = rows > cols (square matrices are
  * not transposed).  Tile granularity g = 64 on the fp32 path; on the bf16 path
  * g = 128 when m <= 128, else 256.  Padded dims are m, n rounded up to g (the
- * padding is zero and leaves the result unchanged).  Matrices with the same
+ * padding is zero and leaves the result unchanged); the GEMM tile is g unless
+ * a tuned entry picks another that divides the padded dims.  Matrices with the same
  * (path, padded m, padded n) share a bucket and run jointly.  Buckets are
  * ordered by executed cost, the sum of 4 m_pad^2 n_pad + 2 m_pad^3 over their
- * members, descending, ties in order of first appearance; members keep input
- * order.  count == 0 gives an empty plan.  Errors: INVALID_ARG for count < 0,
+ * members (or the measured cost, with tuned entries: see dmuon_tune_entry),
+ * descending, ties in order of first appearance; members keep input order.
+ * count == 0 gives an empty plan.  Errors: INVALID_ARG for count < 0,
  * descs == NULL with count > 0, out == NULL, a dim < 1 or an unknown dtype;
  * UNSUPPORTED for a dim >= 2^30, or a side > 2^27 with a bf16 gradient; ALLOC
  * on host allocation failure.
@@ -142,7 +173,10 @@ typedef struct {
 DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
 
 /* muon_plan with options (opts == NULL: the defaults).  INVALID_ARG also for
- * an unknown opts->algo or opts->gram_restart < 0. */
+ * an unknown opts->algo, opts->gram_restart < 0, tuned_count < 0 (or > 0 with
+ * tuned == NULL), or an applied entry with a tile that does not divide the
+ * bucket's padded dims, an unknown algo, the Gram space on the fp32 path, a
+ * negative restart, remap bits beyond the four phases or reserved != 0. */
 DMUON_API dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t count, const dmuon_plan_opts* opts,
                                     dmuon_plan** out);
 
@@ -178,6 +212,32 @@ DMUON_API dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket, 
  * Either pointer may be NULL. */
 DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bucket, int32_t* algo,
                                              int32_t* gram_restart);
+
+/* The configuration a bucket runs with, as a tuning entry (key, tile, algo,
+ * restart, remap bits; cost_ms_per_matrix as given to the plan, else 0). */
+DMUON_API dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t bucket, dmuon_tune_entry* out);
+
+/* Workspace muon_autotune needs for these descs and opts (the largest of its trial plans). */
+DMUON_API dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* descs, int32_t count,
+                                                     const dmuon_plan_opts* opts, size_t* bytes);
+
+/* Measure candidate configurations of every bucket that muon_plan_ex(descs,
+ * count, opts) forms, ignoring opts->tuned, and write the fastest for each into
+ * out[0 .. *out_count) (bucket order of that plan).  Each candidate runs the
+ * bucket's members alone through ns_orthogonalize_batched: one untimed call,
+ * then reps (>= 1) calls timed with HIP events on `stream`.  Candidates: on the
+ * bf16 path tiles 256 (where it divides the padded dims) and 128, remap bits 0,
+ * 4 and 15; the short side, and the Gram space with opts' restart where the
+ * plan options would allow it (forced forms are kept); fp32 buckets have one
+ * candidate.  inputs / outputs: device pointers as for ns_orthogonalize_batched
+ * (trial data; outputs are overwritten).  The call blocks until the trials
+ * are done.  Errors: INVALID_ARG (also out_capacity below the bucket count),
+ * WORKSPACE (below muon_autotune_workspace_bytes), HIP, ALLOC. */
+DMUON_API dmuon_status muon_autotune(const dmuon_matrix_desc* descs, int32_t count, const dmuon_plan_opts* opts,
+                                     const void* const* inputs, void* const* outputs, int32_t ns_steps,
+                                     float a, float b, float c, int32_t reps, void* workspace,
+                                     size_t workspace_bytes, void* stream, dmuon_tune_entry* out,
+                                     int32_t out_capacity, int32_t* out_count);
 
 /* Release a plan (NULL is a no-op). */
 DMUON_API void muon_plan_destroy(dmuon_plan* plan);

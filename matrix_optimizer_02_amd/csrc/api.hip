@@ -93,6 +93,7 @@ hipError_t launch_segs(char* ws, const float* scale, const StepParams& sp, int p
             s.count = (int32_t)bp.members.size();
             s.plan_base = bp.plan_base;
             s.first_iter = ss.first_iter;
+            s.xcd_remap = (int32_t)((bp.xcd_mask >> phase) & 1u);
             s.first_block = ga.total_blocks;
             s.m_pad = bp.m_pad;
             s.n_pad = bp.n_pad;

@@ -19,6 +19,11 @@ constexpr int kPrepTile = 64;
 constexpr std::size_t kAlign = 256;
 // Gram-space iterations between restarts unless the plan options say otherwise.
 constexpr int32_t kDefaultGramRestart = 3;
+// Phases whose launch deals each XCD a contiguous run of a bucket's tiles by
+// default: the B X product (bit 2), whose X panels are then reused in that
+// XCD's L2.
+constexpr uint32_t kDefaultXcdMask = 1u << 2;
+constexpr uint32_t kAllPhasesMask = 0xFu;
 // Longest side a bf16-gradient matrix may have: the bf16 kernels address up
 // to 8 rows of a slab with one 32-bit byte offset per lane.
 constexpr int64_t kMaxBf16Side = int64_t(1) << 27;
@@ -43,6 +48,8 @@ struct BucketPlan {
     int32_t path;          // kPathF32 | kPathBF16
     int32_t algo;          // DMUON_ALGO_SHORT_SIDE | DMUON_ALGO_GRAM_SPACE
     int32_t seg_len;       // iterations per segment: 1 (short side) or the Gram-space restart interval
+    uint32_t xcd_mask;     // bf16: phases (bit per Phase) whose launch deals each XCD a contiguous tile run
+    double cost_ms;        // measured per-matrix cost from a tuned entry, 0 if none
     int32_t tile;          // tile granularity g
     int64_t m_pad, n_pad;
     std::vector<int32_t> members;  // input indices, slot order

@@ -34,11 +34,6 @@
 #include "launch.h"
 #include "tile_map.h"
 
-// which phases deal each XCD a contiguous run of a segment's tiles (bit per
-// phase: 1 Gram, 2 square, 4 B X, 8 prod); 0 keeps the hardware's round-robin
-#ifndef DMUON_XCD_REMAP
-#define DMUON_XCD_REMAP 4
-#endif
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
 #endif
@@ -139,16 +134,9 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 
     // ---- which tile of which matrix --------------------------------------------
     int s, local;
-    if ((DMUON_XCD_REMAP >> PHASE) & 1) {
-        xcd_map((int)blockIdx.x, args.nseg,
-                [&](int i) { return args.seg[i].count * args.seg[i].tiles_per_mat; },
-                [&](int i) { return args.seg[i].first_block; }, s, local);
-    } else {
-        s = 0;
-        for (int i = 1; i < args.nseg; ++i)
-            if ((int)blockIdx.x >= args.seg[i].first_block) s = i;
-        local = (int)blockIdx.x - args.seg[s].first_block;
-    }
+    xcd_map((int)blockIdx.x, args.nseg, [&](int i) { return args.seg[i].count * args.seg[i].tiles_per_mat; },
+            [&](int i) { return args.seg[i].first_block; }, [&](int i) { return args.seg[i].xcd_remap != 0; },
+            s, local);
     const GemmSeg& sg = args.seg[s];
     const int slot = local / sg.tiles_per_mat;
     const int t = local - slot * sg.tiles_per_mat;

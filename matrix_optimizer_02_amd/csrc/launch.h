@@ -72,7 +72,7 @@ struct GemmSeg {
     int32_t count;          // matrices in the bucket
     int32_t plan_base;      // plan index of slot 0
     int32_t first_iter;     // apply the normalisation scale s (Gram s^2, B X s)
-    int32_t pad_;
+    int32_t xcd_remap;      // bf16: each XCD takes a contiguous run of this segment's tiles
     int64_t m_pad, n_pad;
     int64_t p_off, q_off, o_off;  // operand P, operand Q (kProd, kBX), output
     int64_t x_stride, a_stride;   // per-slot bytes

@@ -38,6 +38,8 @@ int32_t tile_granularity(int32_t path, int64_t m) {
 
 bool valid_dtype(int32_t d) { return d == DMUON_F32 || d == DMUON_BF16; }
 
+struct InvalidEntry {};  // a tuned entry that applies to a bucket but cannot run it
+
 }  // namespace
 
 extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t count, const dmuon_plan_opts* opts,
@@ -49,6 +51,8 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
         return DMUON_ERR_INVALID_ARG;
     if (opts && opts->gram_restart < 0) return DMUON_ERR_INVALID_ARG;
     const int32_t restart = opts && opts->gram_restart > 0 ? opts->gram_restart : kDefaultGramRestart;
+    const int32_t ntuned = opts ? opts->tuned_count : 0;
+    if (ntuned < 0 || (ntuned > 0 && opts->tuned == nullptr)) return DMUON_ERR_INVALID_ARG;
     for (int32_t i = 0; i < count; ++i) {
         const dmuon_matrix_desc& d = descs[i];
         if (d.rows < 1 || d.cols < 1 || !valid_dtype(d.grad_dtype) || !valid_dtype(d.param_dtype))
@@ -114,13 +118,47 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
             }
             bp.algo = gram ? DMUON_ALGO_GRAM_SPACE : DMUON_ALGO_SHORT_SIDE;
             bp.seg_len = gram ? restart : 1;
+            bp.xcd_mask = kDefaultXcdMask;
+            bp.cost_ms = 0.0;
+            // a tuned entry for this shape overrides the defaults above
+            const dmuon_tune_entry* e = nullptr;
+            for (int32_t t = 0; t < ntuned && e == nullptr; ++t) {
+                const dmuon_tune_entry& c = opts->tuned[t];
+                if (c.path == bp.path && c.padded_m == bp.m_pad && c.padded_n == bp.n_pad) e = &c;
+            }
+            if (e == nullptr) continue;
+            const bool tile_ok = e->tile == 0 ||
+                                 (bp.path == kPathBF16 ? (e->tile == 128 || e->tile == 256) : e->tile == 64);
+            if (!tile_ok || (e->tile != 0 && (bp.m_pad % e->tile != 0 || bp.n_pad % e->tile != 0)) ||
+                (e->algo != DMUON_ALGO_AUTO && e->algo != DMUON_ALGO_SHORT_SIDE && e->algo != DMUON_ALGO_GRAM_SPACE) ||
+                (e->algo == DMUON_ALGO_GRAM_SPACE && bp.path != kPathBF16) || e->gram_restart < 0 ||
+                (e->xcd_remap != DMUON_XCD_REMAP_DEFAULT && (e->xcd_remap & ~kAllPhasesMask) != 0) ||
+                e->reserved != 0 || !(e->cost_ms_per_matrix >= 0.0))
+                throw InvalidEntry();
+            if (e->tile != 0) bp.tile = e->tile;
+            if (e->algo != DMUON_ALGO_AUTO) {
+                bp.algo = e->algo;
+                bp.seg_len = e->algo == DMUON_ALGO_GRAM_SPACE ? restart : 1;
+            }
+            if (bp.algo == DMUON_ALGO_GRAM_SPACE && e->gram_restart > 0) bp.seg_len = e->gram_restart;
+            if (e->xcd_remap != DMUON_XCD_REMAP_DEFAULT) bp.xcd_mask = e->xcd_remap;
+            bp.cost_ms = e->cost_ms_per_matrix;
         }
-        // order buckets by executed cost, descending; stable sort keeps first appearance on ties
-        for (auto& bp : tmp) bp.exec_cost = (int64_t)bp.members.size() * dense_cost(bp.m_pad, bp.n_pad);
+        // order buckets by executed cost, descending -- measured, when every
+        // bucket has a measured cost, else dense; stable sort keeps first
+        // appearance on ties
+        bool measured = !tmp.empty();
+        for (auto& bp : tmp) {
+            bp.exec_cost = (int64_t)bp.members.size() * dense_cost(bp.m_pad, bp.n_pad);
+            measured = measured && bp.cost_ms > 0.0;
+        }
         std::vector<int32_t> idx(tmp.size());
         for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int32_t)i;
-        std::stable_sort(idx.begin(), idx.end(),
-                         [&](int32_t x, int32_t y) { return tmp[x].exec_cost > tmp[y].exec_cost; });
+        std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+            if (measured)
+                return (double)tmp[x].members.size() * tmp[x].cost_ms > (double)tmp[y].members.size() * tmp[y].cost_ms;
+            return tmp[x].exec_cost > tmp[y].exec_cost;
+        });
         p->buckets.reserve(tmp.size());
         for (int32_t b : idx) p->buckets.push_back(std::move(tmp[b]));
 
@@ -170,6 +208,9 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
     } catch (const std::bad_alloc&) {
         delete p;
         return DMUON_ERR_ALLOC;
+    } catch (const InvalidEntry&) {
+        delete p;
+        return DMUON_ERR_INVALID_ARG;
     }
     *out = p;
     return DMUON_OK;
@@ -225,6 +266,23 @@ extern "C" dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bu
     if (plan == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size()) return DMUON_ERR_INVALID_ARG;
     if (algo) *algo = plan->buckets[bucket].algo;
     if (gram_restart) *gram_restart = plan->buckets[bucket].seg_len;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t bucket, dmuon_tune_entry* out) {
+    if (plan == nullptr || out == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size())
+        return DMUON_ERR_INVALID_ARG;
+    const BucketPlan& bp = plan->buckets[bucket];
+    dmuon_tune_entry e{};
+    e.path = bp.path;
+    e.tile = bp.tile;
+    e.padded_m = bp.m_pad;
+    e.padded_n = bp.n_pad;
+    e.algo = bp.algo;
+    e.gram_restart = bp.seg_len;
+    e.xcd_remap = bp.xcd_mask;
+    e.cost_ms_per_matrix = bp.cost_ms;
+    *out = e;
     return DMUON_OK;
 }
 

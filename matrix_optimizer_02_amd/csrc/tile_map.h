@@ -60,11 +60,15 @@ DMUON_HD void bx_decode_banded(int t, int tn, int tm, int& I, int& J) {
 
 // Block id -> (segment s, tile index within the segment).  Segment s holds
 // total(s) tiles and starts at block first(s) (the running sum).  The
-// hardware deals blocks to XCDs round-robin (XCD = id % 8); segment s's tiles
-// are dealt the same way, continuing where segment s - 1 stopped, but each XCD
-// takes its share of the segment as one contiguous run.
-template <typename Total, typename First>
-DMUON_HD void xcd_map(int bid, int nseg, Total total, First first, int& s, int& local) {
+// hardware deals blocks to XCDs round-robin (XCD = id % 8), and segment s's
+// tiles are dealt the same way, continuing where segment s - 1 stopped: XCD x
+// takes the tiles whose offset rho = (x - first(s)) mod 8 matches, k-th slot
+// after k.  With remap(s) each XCD takes its share of the segment as one
+// contiguous run of tiles (neighbouring tiles share operand panels in that
+// XCD's L2); without it, tile rho + 8 k, which is the plain order
+// local = block - first(s).
+template <typename Total, typename First, typename Remap>
+DMUON_HD void xcd_map(int bid, int nseg, Total total, First first, Remap remap, int& s, int& local) {
     const int x = bid % kXcds;
     int k = bid / kXcds;
     for (s = 0; s < nseg; ++s) {
@@ -73,7 +77,7 @@ DMUON_HD void xcd_map(int bid, int nseg, Total total, First first, int& s, int& 
         const int rho = (x - first(s) % kXcds + kXcds) % kXcds;
         const int share = q + (rho < rem ? 1 : 0);
         if (k < share) {
-            local = rho * q + imin(rho, rem) + k;
+            local = remap(s) ? rho * q + imin(rho, rem) + k : rho + kXcds * k;
             return;
         }
         k -= share;

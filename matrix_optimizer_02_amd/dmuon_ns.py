@@ -11,8 +11,9 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import json
 import os
-from typing import List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import torch  # loads the HIP runtime the library binds to
 
@@ -56,8 +57,32 @@ class AdamWHParams(ctypes.Structure):
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
 
 
+class TuneEntry(ctypes.Structure):
+    """dmuon_tune_entry: how a plan runs a bucket of one (path, padded m, padded n)."""
+    _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("padded_m", ctypes.c_int64),
+                ("padded_n", ctypes.c_int64), ("algo", ctypes.c_int32), ("gram_restart", ctypes.c_int32),
+                ("xcd_remap", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+                ("cost_ms_per_matrix", ctypes.c_double)]
+
+    _KEYS = ("path", "tile", "padded_m", "padded_n", "algo", "gram_restart", "xcd_remap", "cost_ms_per_matrix")
+
+    def to_dict(self) -> dict:
+        return {k: getattr(self, k) for k in self._KEYS}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "TuneEntry":
+        return cls(**{k: d[k] for k in cls._KEYS})
+
+    def __repr__(self):
+        return f"TuneEntry({self.to_dict()})"
+
+
+XCD_REMAP_DEFAULT = 0xFFFFFFFF
+
+
 class PlanOpts(ctypes.Structure):
-    _fields_ = [("algo", ctypes.c_int32), ("gram_restart", ctypes.c_int32)]
+    _fields_ = [("algo", ctypes.c_int32), ("gram_restart", ctypes.c_int32),
+                ("tuned", ctypes.POINTER(TuneEntry)), ("tuned_count", ctypes.c_int32)]
 
 
 # dmuon_algo
@@ -76,6 +101,13 @@ def _load():
         "muon_plan": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, vpp]),
         "muon_plan_ex": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts), vpp]),
         "muon_plan_bucket_algo": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p]),
+        "muon_plan_bucket_config": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(TuneEntry)]),
+        "muon_autotune_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32,
+                                                         ctypes.POINTER(PlanOpts), ctypes.POINTER(ctypes.c_size_t)]),
+        "muon_autotune": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts),
+                                         vpp, vpp, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.POINTER(TuneEntry), ctypes.c_int32, c_int32_p]),
         "muon_plan_workspace_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
         "muon_plan_info": (ctypes.c_int, [ctypes.c_void_p, c_int32_p, c_int32_p]),
         "muon_plan_query": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p,
@@ -153,18 +185,18 @@ class BucketEntry:
 class Plan:
     """Owner of a dmuon_plan (host memory only)."""
 
-    def __init__(self, descs: Sequence[tuple], algo="auto", gram_restart: int = 0):
+    def __init__(self, descs: Sequence[tuple], algo="auto", gram_restart: int = 0,
+                 tuning: Optional[Sequence[TuneEntry]] = None):
         """descs: (rows, cols, grad_dtype, param_dtype); dtypes as torch dtypes,
         "bf16"/"f32" or the DMUON_* codes.  algo: "auto", "short_side" or
         "gram_space" (or the ALGO_* codes); gram_restart: Gram-space
-        iterations between restarts (0: the library's default)."""
+        iterations between restarts (0: the library's default); tuning:
+        per-shape entries (see autotune, load_tuning)."""
         self.descs = [(int(r), int(c), _code(g), _code(p)) for (r, c, g, p) in descs]
-        arr = (MatrixDesc * max(1, len(self.descs)))()
-        for i, (r, c, g, p) in enumerate(self.descs):
-            arr[i] = MatrixDesc(r, c, g, p)
+        arr = _desc_array(self.descs)
         handle = ctypes.c_void_p()
         self._destroy = _lib.muon_plan_destroy
-        opts = PlanOpts(algo if isinstance(algo, int) else _ALGO_CODE[algo], int(gram_restart))
+        opts = _plan_opts(algo, gram_restart, tuning)
         _check(_lib.muon_plan_ex(arr, len(self.descs), ctypes.byref(opts), ctypes.byref(handle)), "muon_plan_ex")
         self._h = handle
 
@@ -203,6 +235,12 @@ class Plan:
                "muon_plan_bucket_algo")
         return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value)
 
+    def config(self, b: int) -> TuneEntry:
+        """The configuration bucket b runs with, as a tuning entry."""
+        e = TuneEntry()
+        _check(_lib.muon_plan_bucket_config(self._h, int(b), ctypes.byref(e)), "muon_plan_bucket_config")
+        return e
+
     def close(self):
         # no module globals here: this also runs from __del__ at interpreter exit
         h = getattr(self, "_h", None)
@@ -214,24 +252,42 @@ class Plan:
         self.close()
 
 
+def _desc_array(descs):
+    arr = (MatrixDesc * max(1, len(descs)))()
+    for i, (r, c, g, p) in enumerate(descs):
+        arr[i] = MatrixDesc(r, c, g, p)
+    return arr
+
+
+def _plan_opts(algo, gram_restart, tuning) -> PlanOpts:
+    opts = PlanOpts(algo if isinstance(algo, int) else _ALGO_CODE[algo], int(gram_restart))
+    if tuning:
+        tab = (TuneEntry * len(tuning))(*tuning)
+        opts.tuned = ctypes.cast(tab, ctypes.POINTER(TuneEntry))
+        opts.tuned_count = len(tuning)
+        opts._keep = tab  # alive for the call
+    return opts
+
+
 def _code(d) -> int:
     if isinstance(d, int):
         return d
     return _DTYPE_CODE[d]
 
 
-def muon_plan(descs: Sequence[tuple], algo="auto", gram_restart: int = 0) -> Plan:
-    return Plan(descs, algo, gram_restart)
+def muon_plan(descs: Sequence[tuple], algo="auto", gram_restart: int = 0,
+              tuning: Optional[Sequence[TuneEntry]] = None) -> Plan:
+    return Plan(descs, algo, gram_restart, tuning)
 
 
 def plan_for(tensors_or_shapes: Sequence, param_dtypes: Optional[Sequence] = None, algo="auto",
-             gram_restart: int = 0) -> Plan:
+             gram_restart: int = 0, tuning: Optional[Sequence[TuneEntry]] = None) -> Plan:
     """Plan from gradient tensors (shape and dtype) and parameter dtypes."""
     descs = []
     for i, g in enumerate(tensors_or_shapes):
         pd = g.dtype if param_dtypes is None else param_dtypes[i]
         descs.append((g.shape[0], g.shape[1], g.dtype, pd))
-    return Plan(descs, algo, gram_restart)
+    return Plan(descs, algo, gram_restart, tuning)
 
 
 def workspace_for(plan: Plan, device=None) -> torch.Tensor:
@@ -304,6 +360,74 @@ def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs
                                        workspace.numel() * workspace.element_size(),
                                        _stream_handle(stream))
     _check(st, "ns_orthogonalize_batched")
+
+
+def autotune(inputs: Sequence[torch.Tensor], out_dtypes: Optional[Sequence] = None, *, algo="auto",
+             gram_restart: int = 0, ns_steps: int = 5, a: float = 3.4445, b: float = -4.7750,
+             c: float = 2.0315, reps: int = 3, stream=None) -> List[TuneEntry]:
+    """muon_autotune on these inputs (trial data, read only): one entry per
+    bucket of the plan they form, the fastest measured configuration.  Output
+    buffers and the workspace are allocated here for the trials.  Blocks."""
+    out_dtypes = out_dtypes or [torch.float32] * len(inputs)
+    descs = [(int(x.shape[0]), int(x.shape[1]), _code(x.dtype), _code(od)) for x, od in zip(inputs, out_dtypes)]
+    for i, x in enumerate(inputs):
+        if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+            raise ValueError(f"inputs[{i}] must be a contiguous 2-D device tensor")
+    arr = _desc_array(descs)
+    opts = _plan_opts(algo, gram_restart, None)
+    need = ctypes.c_size_t()
+    _check(_lib.muon_autotune_workspace_bytes(arr, len(descs), ctypes.byref(opts), ctypes.byref(need)),
+           "muon_autotune_workspace_bytes")
+    dev = inputs[0].device if len(inputs) else None
+    ws = torch.empty(max(1, need.value), dtype=torch.uint8, device=dev)
+    outs = [torch.empty(x.shape, dtype=od, device=x.device) for x, od in zip(inputs, out_dtypes)]
+    nb = Plan(descs, algo, gram_restart).info()[1]
+    res = (TuneEntry * max(1, nb))()
+    got = ctypes.c_int32()
+    i_arr, o_arr = _ptr_array(inputs), _ptr_array(outs)
+    vp = ctypes.POINTER(ctypes.c_void_p)
+    st = _lib.muon_autotune(arr, len(descs), ctypes.byref(opts), ctypes.cast(i_arr, vp), ctypes.cast(o_arr, vp),
+                            int(ns_steps), a, b, c, int(reps), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                            _stream_handle(stream), res, nb, ctypes.byref(got))
+    _check(st, "muon_autotune")
+    return [TuneEntry.from_dict(res[i].to_dict()) for i in range(got.value)]
+
+
+def device_key(device=None) -> str:
+    """Key a tuning cache by the device it was measured on."""
+    p = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
+    return f"{getattr(p, 'gcnArchName', 'unknown')}/{p.name}/{p.multi_processor_count}cu"
+
+
+def save_tuning(entries: Sequence[TuneEntry], path: str, key: Optional[str] = None) -> None:
+    """Merge ``entries`` into the JSON cache at ``path`` under ``key`` (default:
+    the current device); an entry replaces one with the same shape key."""
+    key = key or device_key()
+    data: Dict = {"format": 1, "devices": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    cur = {(e["path"], e["padded_m"], e["padded_n"]): e for e in data["devices"].get(key, [])}
+    for e in entries:
+        cur[(e.path, e.padded_m, e.padded_n)] = e.to_dict()
+    data["devices"][key] = sorted(cur.values(), key=lambda e: (e["path"], e["padded_m"], e["padded_n"]))
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(data, f, indent=1)
+    os.replace(tmp, path)
+
+
+def load_tuning(path: str, key: Optional[str] = None) -> List[TuneEntry]:
+    """The entries cached at ``path`` for ``key`` (default: the current device);
+    [] when the file or the key is absent."""
+    if not os.path.exists(path):
+        return []
+    key = key or device_key()
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("format") != 1:
+        raise ValueError(f"{path}: unknown tuning cache format")
+    return [TuneEntry.from_dict(e) for e in data["devices"].get(key, [])]
 
 
 def adamw_step_batched(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
@@ -400,8 +524,8 @@ class MuonBatch:
     """Convenience owner of a plan and its workspace for a fixed matrix set."""
 
     def __init__(self, grads: Sequence[torch.Tensor], params: Sequence[torch.Tensor], algo="auto",
-                 gram_restart: int = 0):
-        self.plan = plan_for(grads, [p.dtype for p in params], algo, gram_restart)
+                 gram_restart: int = 0, tuning: Optional[Sequence[TuneEntry]] = None):
+        self.plan = plan_for(grads, [p.dtype for p in params], algo, gram_restart, tuning)
         self.workspace = workspace_for(self.plan, grads[0].device if len(grads) else None)
 
     def step(self, grads, momenta, params, **hp):
@@ -415,4 +539,5 @@ __all__ = ["Plan", "PlanEntry", "BucketEntry", "MuonBatch", "DMuonError", "Phase
            "plan_for", "workspace_for", "muon_step_batched", "muon_step_batched_profiled",
            "ns_orthogonalize_batched", "status_string",
            "version", "library_path", "DMUON_F32", "DMUON_BF16", "ALGO_AUTO", "ALGO_SHORT_SIDE",
-           "ALGO_GRAM_SPACE", "PlanOpts"]
+           "ALGO_GRAM_SPACE", "PlanOpts", "TuneEntry", "XCD_REMAP_DEFAULT", "autotune", "device_key",
+           "save_tuning", "load_tuning"]

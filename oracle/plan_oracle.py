@@ -28,11 +28,20 @@ documented contract for that step, written out plainly:
   short-side form otherwise, and always on the f32 path.  A Gram-space bucket
   restarts every ``gram_restart`` iterations (default 3); a short-side bucket
   reports 1.
+* tuned entries (per-shape configurations measured on the device, DMuon
+  explainer on gist.science, sections 2.3 and 2.4): the first entry whose
+  (path, padded m, padded n) matches a bucket sets its tile (which must divide
+  both padded dims; 128 or 256 on bf16, 64 on f32), its form (not the Gram
+  space on f32) and restart, and its XCD remap bits (default: B X only, bit
+  4).  When every bucket carries a measured per-matrix cost > 0, buckets are
+  ordered by count times that cost instead of the dense cost.
 """
 
 from __future__ import annotations
 
 DEFAULT_GRAM_RESTART = 3
+DEFAULT_XCD_REMAP = 4  # bit per phase: 1 Gram, 2 square, 4 B X, 8 prod
+XCD_REMAP_DEFAULT = 0xFFFFFFFF
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -64,7 +73,37 @@ def bucket_algo(path: str, m_pad: int, n_pad: int, shapes, option: str = "auto")
     return "short_side"
 
 
-def plan_reference(descs, algo: str = "auto", gram_restart: int = 0):
+def _apply_entry(bucket, e, option_restart):
+    """Apply tuned entry e (dict with the library's field names and codes:
+    path 0/1, algo 0 auto / 1 short side / 2 Gram space) to bucket."""
+    tile = e.get("tile", 0)
+    allowed = (128, 256) if bucket["path"] == "bf16" else (64,)
+    if tile and (tile not in allowed or bucket["m_pad"] % tile or bucket["n_pad"] % tile):
+        raise ValueError("tile")
+    forms = {0: None, 1: "short_side", 2: "gram_space"}
+    if e.get("algo", 0) not in forms:
+        raise ValueError("algo")
+    form = forms[e.get("algo", 0)]
+    if form == "gram_space" and bucket["path"] != "bf16":
+        raise ValueError("gram space on f32")
+    if e.get("gram_restart", 0) < 0 or e.get("cost_ms_per_matrix", 0.0) < 0:
+        raise ValueError("negative")
+    remap = e.get("xcd_remap", XCD_REMAP_DEFAULT)
+    if remap != XCD_REMAP_DEFAULT and remap & ~0xF:
+        raise ValueError("remap bits")
+    if tile:
+        bucket["tile"] = tile
+    if form is not None:
+        bucket["algo"] = form
+        bucket["gram_restart"] = option_restart if form == "gram_space" else 1
+    if bucket["algo"] == "gram_space" and e.get("gram_restart", 0) > 0:
+        bucket["gram_restart"] = e["gram_restart"]
+    if remap != XCD_REMAP_DEFAULT:
+        bucket["xcd_remap"] = remap
+    bucket["cost"] = e.get("cost_ms_per_matrix", 0.0)
+
+
+def plan_reference(descs, algo: str = "auto", gram_restart: int = 0, tuned=None):
     """descs: list of (rows, cols, grad_dtype, param_dtype) with dtype codes
     0 = fp32, 1 = bf16.  Returns a list of per-matrix dicts with keys
     bucket, slot, transposed, m, n, m_pad, n_pad, cost, and the list of
@@ -89,14 +128,27 @@ def plan_reference(descs, algo: str = "auto", gram_restart: int = 0):
         items.append({"transposed": r > c, "m": m, "n": n, "m_pad": key[1],
                       "n_pad": key[2], "cost": _cost(m, n), "key": key})
     first_seen = {k: i for i, k in enumerate(keys_in_order)}
-    order = sorted(keys_in_order,
-                   key=lambda k: (-len(members[k]) * _cost(k[1], k[2]), first_seen[k]))
+    info = {}
+    for key in keys_in_order:
+        form = bucket_algo(key[0], key[1], key[2], [(items[i]["m"], items[i]["n"]) for i in members[key]], algo)
+        bk = {"path": key[0], "m_pad": key[1], "n_pad": key[2], "members": list(members[key]),
+              "algo": form, "gram_restart": restart if form == "gram_space" else 1,
+              "tile": tile_granularity(key[0], key[1]), "xcd_remap": DEFAULT_XCD_REMAP, "cost": 0.0}
+        code = DTYPE_BF16 if key[0] == "bf16" else DTYPE_F32
+        for e in tuned or []:
+            if (e["path"], e["padded_m"], e["padded_n"]) == (code, key[1], key[2]):
+                _apply_entry(bk, e, restart)
+                break
+        info[key] = bk
+    measured = bool(keys_in_order) and all(info[k]["cost"] > 0 for k in keys_in_order)
+    if measured:
+        order = sorted(keys_in_order, key=lambda k: (-len(members[k]) * info[k]["cost"], first_seen[k]))
+    else:
+        order = sorted(keys_in_order, key=lambda k: (-len(members[k]) * _cost(k[1], k[2]), first_seen[k]))
     buckets = []
     for b, key in enumerate(order):
         for slot, idx in enumerate(members[key]):
             items[idx]["bucket"] = b
             items[idx]["slot"] = slot
-        form = bucket_algo(key[0], key[1], key[2], [(items[i]["m"], items[i]["n"]) for i in members[key]], algo)
-        buckets.append({"path": key[0], "m_pad": key[1], "n_pad": key[2], "members": list(members[key]),
-                        "algo": form, "gram_restart": restart if form == "gram_space" else 1})
+        buckets.append(info[key])
     return items, buckets

@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol():
     raw = ctypes.CDLL(d.library_path())
     names = build_mod.exported_symbols()
     assert set(names) == {"muon_plan", "muon_plan_ex", "muon_plan_workspace_bytes", "muon_plan_info",
-                          "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_destroy",
+                          "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_bucket_config",
+                          "muon_autotune_workspace_bytes", "muon_autotune", "muon_plan_destroy",
                           "muon_step_batched",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
@@ -96,6 +97,98 @@ def test_default_algo_by_hand():
     p = d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)])
     assert p.info()[1] == 1 and p.bucket(0).algo == d.ALGO_SHORT_SIDE
     assert d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)], "gram_space").bucket(0).algo == d.ALGO_GRAM_SPACE
+
+
+def _entry(path, m_pad, n_pad, tile=0, algo=0, restart=0, remap=0xFFFFFFFF, cost=0.0):
+    return {"path": path, "padded_m": m_pad, "padded_n": n_pad, "tile": tile, "algo": algo,
+            "gram_restart": restart, "xcd_remap": remap, "cost_ms_per_matrix": cost}
+
+
+TUNED_CASES = {
+    # tile, form, restart and remap overrides on some buckets, dense-cost order kept
+    "overrides": (CASES["mixed_odd"], [_entry(1, 512, 768, tile=128, remap=15), _entry(1, 256, 256, algo=2, restart=2),
+                                       _entry(1, 4096, 14336, algo=1, remap=0), _entry(0, 256, 512, tile=64),
+                                       _entry(1, 128, 640, restart=5), _entry(1, 999, 999, tile=128)]),
+    # every bucket measured: ordered by count x cost, ties by first appearance
+    "measured_order": ([(256, 512, 1, 1), (1024, 4096, 1, 1), (256, 512, 1, 1), (128, 128, 1, 1), (64, 64, 0, 0)],
+                       [_entry(1, 256, 512, cost=2.0), _entry(1, 1024, 4096, cost=1.0), _entry(1, 128, 128, cost=4.0),
+                        _entry(0, 64, 64, cost=4.0)]),
+    # one bucket unmeasured: dense-cost order
+    "partly_measured": ([(256, 512, 1, 1), (1024, 4096, 1, 1), (128, 128, 1, 1)],
+                        [_entry(1, 256, 512, cost=9.0), _entry(1, 128, 128, cost=9.0)]),
+}
+
+
+def _tune_entries(es):
+    return [d.TuneEntry.from_dict(e) for e in es]
+
+
+@pytest.mark.parametrize("name", sorted(TUNED_CASES))
+def test_tuned_plan_matches_reference(name):
+    descs, es = TUNED_CASES[name]
+    items, buckets = plan_reference(descs, tuned=es)
+    p = d.Plan(descs, tuning=_tune_entries(es))
+    assert p.info() == (len(descs), len(buckets))
+    for i, it in enumerate(items):
+        e = p.query(i)
+        assert (e.bucket, e.slot) == (it["bucket"], it["slot"]), i
+    for b, bk in enumerate(buckets):
+        c = p.config(b)
+        assert (c.path, c.padded_m, c.padded_n) == (0 if bk["path"] == "f32" else 1, bk["m_pad"], bk["n_pad"])
+        assert (c.tile, c.algo, c.gram_restart, c.xcd_remap) == (
+            bk["tile"], ALGO[bk["algo"]], bk["gram_restart"], bk["xcd_remap"]), b
+        assert c.cost_ms_per_matrix == bk["cost"]
+        assert p.bucket(b).tile == bk["tile"]
+
+
+@pytest.mark.parametrize("bad", [_entry(1, 512, 768, tile=64), _entry(1, 128, 640, tile=256),
+                                 _entry(1, 512, 768, tile=384), _entry(0, 256, 512, tile=128),
+                                 _entry(0, 256, 512, algo=2), _entry(1, 512, 768, algo=3),
+                                 _entry(1, 512, 768, restart=-1), _entry(1, 512, 768, remap=16),
+                                 _entry(1, 512, 768, cost=-1.0)])
+def test_invalid_tuned_entries_rejected(bad):
+    descs = CASES["mixed_odd"]
+    with pytest.raises(ValueError):
+        plan_reference(descs, tuned=[bad])
+    with pytest.raises(d.DMuonError) as e:
+        d.Plan(descs, tuning=_tune_entries([bad]))
+    assert e.value.status == d.DMUON_ERR_INVALID_ARG
+    # the same entry on a shape no bucket has is ignored
+    d.Plan([(8, 8, 1, 1)], tuning=_tune_entries([bad])).close()
+
+
+def test_tuning_cache_round_trip(tmp_path):
+    path = str(tmp_path / "tune.json")
+    assert d.load_tuning(path, key="devA") == []
+    a = _tune_entries([_entry(1, 4096, 14336, tile=256, algo=2, restart=3, remap=4, cost=2.5),
+                       _entry(1, 256, 1536, tile=128, algo=1, restart=1, remap=15, cost=0.25)])
+    d.save_tuning(a, path, key="devA")
+    d.save_tuning(_tune_entries([_entry(0, 64, 64, tile=64, algo=1, restart=1, remap=4, cost=0.01)]), path,
+                  key="devB")
+    # a later entry for the same shape replaces the earlier one
+    d.save_tuning(_tune_entries([_entry(1, 256, 1536, tile=256, algo=2, restart=3, remap=0, cost=0.2)]), path,
+                  key="devA")
+    got = {(e.padded_m, e.padded_n): e.to_dict() for e in d.load_tuning(path, key="devA")}
+    assert got[(4096, 14336)] == a[0].to_dict()
+    assert got[(256, 1536)]["tile"] == 256 and got[(256, 1536)]["cost_ms_per_matrix"] == 0.2
+    assert [e.padded_m for e in d.load_tuning(path, key="devB")] == [64]
+    assert d.load_tuning(path, key="devC") == []
+
+
+def test_autotune_argument_errors():
+    need = ctypes.c_size_t()
+    arr = (d.MatrixDesc * 1)(d.MatrixDesc(256, 512, 1, 1))
+    assert LIB.muon_autotune_workspace_bytes(arr, 1, None, None) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_autotune_workspace_bytes(arr, 1, None, ctypes.byref(need)) == d.DMUON_OK
+    # the trial plans include the Gram-space one, whose workspace is the largest
+    assert need.value >= d.Plan([(256, 512, 1, 1)], "gram_space").workspace_bytes()
+    got = ctypes.c_int32()
+    res = (d.TuneEntry * 1)()
+    for reps, cap in ((0, 1), (1, 0)):
+        assert LIB.muon_autotune(arr, 1, None, _arr([8]), _arr([16]), 5, 3.4445, -4.775, 2.0315, reps, None, 0,
+                                 None, res, cap, ctypes.byref(got)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_autotune(arr, 1, None, _arr([8]), _arr([16]), 5, 3.4445, -4.775, 2.0315, 1, None, 0,
+                             None, res, 1, ctypes.byref(got)) == d.DMUON_ERR_WORKSPACE
 
 
 def test_workspace_covers_operands():

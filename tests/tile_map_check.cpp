@@ -40,7 +40,7 @@ int check_bx(int tn, int tm) {
     return (int)seen.size() == tn * tm ? 0 : fail("bx coverage", tn, tm);
 }
 
-int check_launch(const std::vector<int>& totals) {
+int check_launch(const std::vector<int>& totals, const std::vector<int>& remap) {
     std::vector<int> first(totals.size());
     int sum = 0;
     for (size_t s = 0; s < totals.size(); ++s) {
@@ -53,7 +53,9 @@ int check_launch(const std::vector<int>& totals) {
     for (int b = 0; b < sum; ++b) {
         int s, local;
         xcd_map(b, (int)totals.size(), [&](int i) { return totals[i]; }, [&](int i) { return first[i]; },
-                s, local);
+                [&](int i) { return remap[i] != 0; }, s, local);
+        // a segment left in the hardware's order maps block b to tile b - first(s)
+        if (s >= 0 && s < (int)totals.size() && !remap[s] && local != b - first[s]) return fail("plain order", b, s);
         if (s < 0 || s >= (int)totals.size() || local < 0 || local >= totals[s]) return fail("map range", b, s);
         if (!seen.insert({s, local}).second) return fail("map duplicate", b, s);
         runs[s][b % kXcds].push_back(local);
@@ -63,8 +65,9 @@ int check_launch(const std::vector<int>& totals) {
         int lo = 1 << 30, hi = 0;
         for (int x = 0; x < kXcds; ++x) {
             const auto& r = runs[s][x];
+            const int step = remap[s] ? 1 : kXcds;  // contiguous run, or every 8th tile
             for (size_t i = 1; i < r.size(); ++i)
-                if (r[i] != r[i - 1] + 1) return fail("run not contiguous", (int)s, x);
+                if (r[i] != r[i - 1] + step) return fail("run not contiguous", (int)s, x);
             lo = std::min(lo, (int)r.size());
             hi = std::max(hi, (int)r.size());
         }
@@ -81,12 +84,16 @@ int main() {
     const std::vector<std::vector<int>> launches = {
         {1}, {7}, {8}, {9}, {136 * 12, 136 * 8, 10 * 8}, {896 * 12, 256 * 8, 64 * 8},
         {3, 5, 7, 11, 13}, {1, 1, 1, 1, 1, 1, 1, 1, 1}, {21 * 56, 1 * 56, 6 * 84}, {105 * 28, 74 * 14 * 84}};
-    for (const auto& l : launches) bad |= check_launch(l);
+    for (const auto& l : launches) {
+        bad |= check_launch(l, std::vector<int>(l.size(), 1));
+        bad |= check_launch(l, std::vector<int>(l.size(), 0));
+    }
     std::srand(7);
-    for (int trial = 0; trial < 200; ++trial) {
-        std::vector<int> l(1 + std::rand() % 6);
+    for (int trial = 0; trial < 400; ++trial) {
+        std::vector<int> l(1 + std::rand() % 6), r(l.size());
         for (auto& v : l) v = 1 + std::rand() % 700;
-        bad |= check_launch(l);
+        for (auto& v : r) v = std::rand() % 2;  // mixed orders in one launch
+        bad |= check_launch(l, r);
     }
     std::printf(bad ? "FAILED\n" : "OK\n");
     return bad;
