@@ -21,9 +21,13 @@
 // "Benutting van Symmetrie"); matrices of similar shapes run jointly to keep
 // the GPU occupied and amortise dispatch (same section, "Batching").
 //
-// Tile: T x T outputs per 256-thread workgroup (T = 256 or 128), 4 waves in a
-// 2 x 2 grid, each wave (T/2) x (T/2) outputs as (T/64)^2 blocks of
-// v_mfma_f32_32x32x16_bf16.  K is staged through LDS in 64-deep slabs, two
+// Tile: T x T outputs per workgroup (T = 256 or 128).  T = 256: 8 waves in a
+// 2 x 4 grid, two per SIMD, each 128 x 64 outputs as 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 (128 accumulator registers, so two waves fit a
+// SIMD and one wave's fragment reads and loads overlap the other's MFMAs).
+// T = 128: 4 waves in a 2 x 2 grid, each 64 x 64.  Every output element is
+// accumulated by one wave in the same k order either way.  K is staged
+// through LDS in 64-deep slabs, two
 // stages, by direct global->LDS loads; 16-byte chunks are XOR-swizzled by row
 // so that the fragment reads hit distinct banks.  Each MFMA k-step is its own
 // scheduling region: its MFMAs interleaved with the next k-step's fragment
@@ -41,11 +45,12 @@
 #define DMUON_SPREAD 1
 #endif
 // ends of the first and second load pieces, in eighths of a slab's loads
+// (-1: the tile configuration's own split)
 #ifndef DMUON_PIECE1
-#define DMUON_PIECE1 3
+#define DMUON_PIECE1 -1
 #endif
 #ifndef DMUON_PIECE2
-#define DMUON_PIECE2 6
+#define DMUON_PIECE2 -1
 #endif
 #ifndef DMUON_ROTATE_K
 #define DMUON_ROTATE_K 1
@@ -65,11 +70,21 @@ constexpr int kChunks = kRowBytes / 16;     // 16-byte chunks per such row
 constexpr int kDmaRows = 1024 / kRowBytes;  // rows one 1 KB wave load fills
 constexpr int KS = kBK / 16;                // MFMA k-steps per slab
 
+// T = 256: 8 waves in a 2 x 4 grid, each 128 x 64 outputs, two waves per
+// SIMD; T = 128: 4 waves in a 2 x 2 grid, each 64 x 64.
 template <int T>
 struct TileCfg {
-    static constexpr int WT = T / 2;               // wave tile
-    static constexpr int F = WT / 32;              // MFMA blocks per wave per dim
-    static constexpr int kDmaPerOp = T * kRowBytes / 1024 / 4;  // 1 KB loads per wave per operand per slab
+    static constexpr int NW = T == 256 ? 8 : 4;    // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int WC = NW / 2;              // waves across the tile's columns (2 down its rows)
+    static constexpr int RW = T / 2, CW = T / WC;  // rows, columns of one wave's sub-tile
+    static constexpr int FI = RW / 32, FJ = CW / 32;  // MFMA blocks per wave per dim
+    static constexpr int kDmaPerOp = T * kRowBytes / 1024 / NW;  // 1 KB loads per wave per operand per slab
+    // A slab's loads in pieces ending at these eighths (measured: with two
+    // waves per SIMD, half right after the barrier and half in the first
+    // k-step; with one, 3/8, 3/8 and 2/8 over the barrier and two k-steps).
+    static constexpr int kPiece1Eighths = DMUON_PIECE1 >= 0 ? DMUON_PIECE1 : (NW == 8 ? 4 : 3);
+    static constexpr int kPiece2Eighths = DMUON_PIECE2 >= 0 ? DMUON_PIECE2 : (NW == 8 ? 8 : 6);
     static constexpr int kOperandBytes = T * kRowBytes;
     static constexpr int kStageBytes = 2 * kOperandBytes;
     // B X: the P slab is kBK rows (k) of T long-side values
@@ -127,7 +142,7 @@ template <int T>
 __device__ __forceinline__ int swizzle_e(int r) { return r & (T / 8 - 1); }
 
 template <int T, int PHASE>
-__global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
+__global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
     static_assert(2 * C::kStageBytes >= T * C::kERowBytes, "epilogue tile fits the stages");
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / C::WC, wc = wave % C::WC;
 
     // ---- global -> LDS (direct) ----------------------------------------------------
     // One global_load_lds_dwordx4 of a wave fills 1 KB of LDS: lane l writes
@@ -237,34 +252,34 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     // that frees its stage, the other two inside the next two k-steps, so the
     // address unit never takes a whole slab's loads at once while the matrix
     // pipe waits behind them.
-    constexpr int kPiece1 = DMUON_SPREAD ? (DMUON_PIECE1 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
-    constexpr int kPiece2 = DMUON_SPREAD ? (DMUON_PIECE2 * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kPiece1 = DMUON_SPREAD ? (C::kPiece1Eighths * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kPiece2 = DMUON_SPREAD ? (C::kPiece2Eighths * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
 
-    floatx16 acc[C::F][C::F];
+    floatx16 acc[C::FI][C::FJ];
     #pragma unroll
-    for (int i = 0; i < C::F; ++i)
+    for (int i = 0; i < C::FI; ++i)
         #pragma unroll
-        for (int j = 0; j < C::F; ++j)
+        for (int j = 0; j < C::FJ; ++j)
             #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int lrow = lane & 31, khalf = lane >> 5;
     const int swz = swizzle(lrow);  // fragment rows start at multiples of 32
-    const int a_row0 = (wr * C::WT + lrow) * kRowBytes;
-    const int b_row0 = (wc * C::WT + lrow) * kRowBytes;
+    const int a_row0 = (wr * C::RW + lrow) * kRowBytes;
+    const int b_row0 = (wc * C::CW + lrow) * kRowBytes;
     // B X transposing read: lane 16 g + s of a 16-lane group g addresses row
     // (s / 4) and columns 4 (s % 4) .. + 3 of a 4 x 16 block; it receives that
     // block's column s, i.e. 4 consecutive k of output row jbase + s.
     const int tr_g = lane >> 4, tr_s = lane & 15;
     const int tr_row = 8 * (tr_g >> 1) + (tr_s >> 2);                 // + 16 ks + 4 half
-    const int tr_col = wr * C::WT + 16 * (tr_g & 1) + 4 * (tr_s & 3);  // + 32 fi
+    const int tr_col = wr * C::RW + 16 * (tr_g & 1) + 4 * (tr_s & 3);  // + 32 fi
     const int tr_sw = swizzle_p(tr_s >> 2);                           // rows are 4-aligned
-    bf16x8 fa[2][C::F], fb[2][C::F];
+    bf16x8 fa[2][C::FI], fb[2][C::FJ];
 
 #define DMUON_READ_A(BUF, BASE, KS_)                                                              \
     do {                                                                                          \
         if (PHASE == kBX) {                                                                       \
-            _Pragma("unroll") for (int i_ = 0; i_ < C::F; ++i_) {                                 \
+            _Pragma("unroll") for (int i_ = 0; i_ < C::FI; ++i_) {                                \
                 shortx4 h_[2];                                                                    \
                 _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) {                                \
                     const int r_ = 16 * (KS_) + 4 * t_ + tr_row;                                  \
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
             }                                                                                     \
         } else {                                                                                  \
             const int pc_ = ((((KS_) * 2 + khalf) ^ swz) << 4);                                   \
-            _Pragma("unroll") for (int i_ = 0; i_ < C::F; ++i_)                                   \
+            _Pragma("unroll") for (int i_ = 0; i_ < C::FI; ++i_)                                  \
                 fa[BUF][i_] = *reinterpret_cast<const bf16x8*>((BASE) + a_row0 + i_ * 32 * kRowBytes + pc_); \
         }                                                                                         \
     } while (0)
@@ -286,20 +301,20 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     do {                                                                                          \
         DMUON_READ_A(BUF, BASE, KS_);                                                             \
         const int pc_ = ((((KS_) * 2 + khalf) ^ swz) << 4);                                       \
-        _Pragma("unroll") for (int j_ = 0; j_ < C::F; ++j_)                                       \
+        _Pragma("unroll") for (int j_ = 0; j_ < C::FJ; ++j_)                                      \
             fb[BUF][j_] = *reinterpret_cast<const bf16x8*>((BASE) + C::kOperandBytes + b_row0 +     \
                                                            j_ * 32 * kRowBytes + pc_);            \
     } while (0)
 #define DMUON_MFMA(BUF)                                                                           \
     do {                                                                                          \
-        _Pragma("unroll") for (int i_ = 0; i_ < C::F; ++i_)                                       \
-            _Pragma("unroll") for (int j_ = 0; j_ < C::F; ++j_)                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < C::FI; ++i_)                                      \
+            _Pragma("unroll") for (int j_ = 0; j_ < C::FJ; ++j_)                                  \
                 acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUF][i_], fb[BUF][j_],   \
                                                                       acc[i_][j_], 0, 0, 0);      \
     } while (0)
 
-    constexpr int NREAD = (PHASE == kBX ? 3 : 2) * C::F;  // fragment reads per k-step
-    constexpr int NMFMA = C::F * C::F;                    // MFMAs per k-step
+    constexpr int NREAD = (PHASE == kBX ? 2 : 1) * C::FI + C::FJ;  // fragment reads per k-step
+    constexpr int NMFMA = C::FI * C::FJ;                          // MFMAs per k-step
     constexpr int NV1 = 2 * (kPiece2 - kPiece1);          // loads of piece 1 (k-step 0)
     constexpr int NV2 = 2 * (C::kDmaPerOp - kPiece2);     // loads of piece 2 (k-step 1)
     // One k-step as its own scheduling region: each of the first MFMAs is
@@ -379,15 +394,15 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 #undef DMUON_MFMA
 
     // ---- epilogue -----------------------------------------------------------------
-    // acc[i][j][v] holds output row  wr*WT + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4
-    //                  and column  wc*WT + 32 j + lane % 32   of the T x T tile,
+    // acc[i][j][v] holds output row  wr*RW + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4
+    //                  and column  wc*CW + 32 j + lane % 32   of the T x T tile,
     // i.e. four consecutive rows r0 .. r0 + 3 of one column c per (i, j, v / 4).
     // The tile goes through LDS transposed, as E[c][r] = C[r][c]: each lane's
     // four values are one 8-byte piece of a row of E.
     const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
     // T rows of 2 T bytes from global (row stride ld elements) into E, whole.
     auto load_tile = [&](const uint16_t* src, int64_t ld) {
-        constexpr int kLoads = T * C::kERowBytes / 1024 / 4;  // 1 KB loads per wave
+        constexpr int kLoads = T * C::kERowBytes / 1024 / C::NW;  // 1 KB loads per wave
         #pragma unroll 8
         for (int i = 0; i < kLoads; ++i) {
             const int q = wave * kLoads + i;
@@ -404,10 +419,10 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     };
     // E rows to global rows (row stride ld elements), whole 16-byte chunks.
     auto store_rows = [&](uint16_t* dst, int64_t ld) {
-        constexpr int kStores = T * C::kEChunks / 256;
+        constexpr int kStores = T * C::kEChunks / C::NT;
         #pragma unroll 8
         for (int i = 0; i < kStores; ++i) {
-            const int q = tid + 256 * i;
+            const int q = tid + C::NT * i;
             const int row = q / C::kEChunks, lc = q % C::kEChunks;
             const uint4 v = *reinterpret_cast<const uint4*>(smem + row * C::kERowBytes +
                                                             ((lc ^ swizzle_e<T>(row)) << 4));
@@ -424,8 +439,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         const int g = lane >> 4, i16 = lane & 15, k = i16 >> 2, q = i16 & 3;
         constexpr int kRowBlocks = T / 16, kColBlocks = T / 32;
         #pragma unroll 4
-        for (int it = 0; it < kRowBlocks * kColBlocks / 4; ++it) {
-            const int w = 4 * it + wave;
+        for (int it = 0; it < kRowBlocks * kColBlocks / C::NW; ++it) {
+            const int w = C::NW * it + wave;
             const int r0 = (w % kRowBlocks) * 16, cb = (w / kRowBlocks) * 32 + 8 * g;
             shortx4 h[2];
             #pragma unroll
@@ -445,13 +460,13 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + slot * sg.x_stride) +
                        (int64_t)J * T * ldn + (int64_t)I * T;
         #pragma unroll
-        for (int i = 0; i < C::F; ++i)
+        for (int i = 0; i < C::FI; ++i)
             #pragma unroll
-            for (int j = 0; j < C::F; ++j)
+            for (int j = 0; j < C::FJ; ++j)
                 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4) {
-                    const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
-                    const int c = wc * C::WT + j * 32 + lrow;
+                    const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * khalf;
+                    const int c = wc * C::CW + j * 32 + lrow;
                     uint2 o;
                     o.x = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 0]) |
                           ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 1]) << 16);
@@ -473,13 +488,13 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
         const float beta = args.b;
         if (PHASE == kSquare) load_tile(P + (int64_t)J * T * ld + (int64_t)I * T, ld);
         #pragma unroll
-        for (int i = 0; i < C::F; ++i)
+        for (int i = 0; i < C::FI; ++i)
             #pragma unroll
-            for (int j = 0; j < C::F; ++j)
+            for (int j = 0; j < C::FJ; ++j)
                 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4) {
-                    const int r0 = wr * C::WT + i * 32 + 8 * v4 + 4 * khalf;
-                    const int c = wc * C::WT + j * 32 + lrow;
+                    const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * khalf;
+                    const int c = wc * C::CW + j * 32 + lrow;
                     char* p = e_ptr(c, r0);
                     float v[4];
                     #pragma unroll
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
 
 template <int T>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.total_blocks), block(256);
+    const dim3 grid((unsigned)a.total_blocks), block(TileCfg<T>::NT);
     switch (a.phase) {
         case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram>), grid, block, 0, stream, a); break;
         case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare>), grid, block, 0, stream, a); break;
