@@ -58,6 +58,19 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
     T* X = reinterpret_cast<T*>(a.ws + r.x_off0);
     const float beta = a.beta;
     float ss = 0.f;
+    // every row's loads first, so that all of them are in flight at once (the
+    // stores below could alias them as far as the compiler knows)
+    float4 gv[4], mv[4];
+    if (VEC) {
+        #pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int64_t rho = rho0 + rr + 16 * p, kap = kap0 + 4 * cg;
+            if (rho < r.rows && kap < r.cols) {
+                gv[p] = load4(G + rho * r.cols + kap);
+                if (a.has_momentum) mv[p] = load4(M + rho * r.cols + kap);
+            }
+        }
+    }
     #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int row = rr + 16 * p;
@@ -68,10 +81,10 @@ __device__ __forceinline__ void prep_tile(const PrepArgs& a, const DevMatRec& r,
             const int64_t e = rho * r.cols + kap;
             if (VEC) {
                 if (kap < r.cols) {
-                    const float4 g = load4(G + e);
+                    const float4 g = gv[p];
                     float4 uu = g;
                     if (a.has_momentum) {
-                        const float4 m = load4(M + e);
+                        const float4 m = mv[p];
                         float4 mn;
                         mn.x = fmaf(beta, m.x, g.x);
                         mn.y = fmaf(beta, m.y, g.y);

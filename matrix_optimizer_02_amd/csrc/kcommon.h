@@ -33,19 +33,44 @@ template <> struct Elem<uint16_t> {
     __device__ static __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
-// Four consecutive elements <-> float4 (aligned to 4 elements).
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// Streaming vector accesses for the bandwidth-bound passes, which touch every
+// byte once: non-temporal loads and stores (measured on a 4 GiB copy: 6.07
+// TB/s against 5.73 with ordinary accesses).
+#ifndef DMUON_NT
+#define DMUON_NT 1
+#endif
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ V ld_stream(const void* p) {
+    const V* q = reinterpret_cast<const V*>(p);
+    if (DMUON_NT) return __builtin_nontemporal_load(q);
+    return *q;
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(void* p, V v) {
+    V* q = reinterpret_cast<V*>(p);
+    if (DMUON_NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
+// Four consecutive elements <-> float4 (aligned to 4 elements), streaming.
+__device__ __forceinline__ float4 load4(const float* p) {
+    const f32x4_t v = ld_stream<f32x4_t>(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ float4 load4(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const u32x2_t u = ld_stream<u32x2_t>(p);
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
-__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(float* p, float4 v) { st_stream<f32x4_t>(p, f32x4_t{v.x, v.y, v.z, v.w}); }
 __device__ __forceinline__ void store4(uint16_t* p, float4 v) {
-    uint2 u;
+    u32x2_t u;
     u.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
     u.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
+    st_stream<u32x2_t>(p, u);
 }
 
 // Largest i in [0, n) with key(i) <= x, for a non-decreasing key (key(0) <= x).
