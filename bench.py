@@ -23,7 +23,9 @@ events at its launch boundaries inside the timed steps.
 momentum, cast and norm partials; apply: the update) in GB/s of their required
 traffic against the 8 TB/s HBM peak.  ``adamw`` times the AdamW companion
 step on Llama-3.1-8B's non-Muon parameters (one GPU's 1/8 element share) the
-same way.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+same way.  ``graph`` replays the same step from a HIP graph (no host enqueueing
+in the timed span; the number that matters for small, launch-bound
+workloads).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
 the same workload.
 """
 
@@ -119,6 +121,32 @@ def cpu_baseline(w, host_samples):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": "full fp64 oracle Muon step on " + ", ".join(names) + f" ({dt:.1f} s)",
             "seconds": dt}
+
+
+def graph_bench(d, plan, G, M, W, ws, reps: int, count: int):
+    """The same step captured once in a HIP graph and replayed: no host
+    enqueueing in the timed span, which is what small, launch-bound workloads
+    need.  Timed with HIP events around the replays on the current stream."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"replays": reps, "ms_per_step": round(ms, 4), "matrices_per_s": round(count / (ms / 1e3), 2)}
 
 
 def adamw_bench(d, dev, steps: int = 10, warmup: int = 2):
@@ -312,6 +340,7 @@ def main(argv=None):
                   "gbps": round(apply_bytes / (avg["apply"] / 1e3) / 1e9, 1),
                   "frac_hbm": round(apply_bytes / (avg["apply"] / 1e3) / HBM_PEAK_BPS, 4)},
     }
+    out["graph"] = graph_bench(d, plan, G, M, W, ws, max(args.steps, 50 if ms_per_step < 5 else 0), w.count)
     if tuning_info is not None:
         out["tuning"] = tuning_info
     if not args.no_adamw:
