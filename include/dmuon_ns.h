@@ -167,7 +167,8 @@ typedef struct {
  * descending, ties in order of first appearance; members keep input order.
  * count == 0 gives an empty plan.  Errors: INVALID_ARG for count < 0,
  * descs == NULL with count > 0, out == NULL, a dim < 1 or an unknown dtype;
- * UNSUPPORTED for a dim >= 2^30, or a side > 2^27 with a bf16 gradient; ALLOC
+ * UNSUPPORTED for a dim >= 2^30, a side > 2^27 with a bf16 gradient, or a
+ * bucket whose B X launch would need more than 2^31 - 1 tiles; ALLOC
  * on host allocation failure.
  * On success *out owns the plan; release it with muon_plan_destroy. */
 DMUON_API dmuon_status muon_plan(const dmuon_matrix_desc* descs, int32_t count, dmuon_plan** out);
@@ -322,7 +323,8 @@ DMUON_API dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const 
                                                   size_t workspace_bytes, void* stream,
                                                   void* const* events, int32_t num_events);
 
-/* Events muon_step_batched_profiled records: 3 + 4 ns_steps (-1 if ns_steps < 0). */
+/* Events muon_step_batched_profiled records: 3 + 4 ns_steps (-1 if ns_steps < 0 or
+ * the count would not fit an int32). */
 DMUON_API int32_t muon_step_event_count(int32_t ns_steps);
 
 /* Create n HIP events (timing enabled) into events[0..n); the caller destroys

@@ -7,8 +7,10 @@
 // No device memory is allocated and nothing is synchronised: everything is
 // enqueued on the caller's stream.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
+#include <new>
 #include <utility>
 #include <vector>
 
@@ -82,7 +84,9 @@ hipError_t launch_segs(char* ws, const float* scale, const StepParams& sp, int p
         for (const SegSpec& ss : segs) {
             const BucketPlan& bp = *ss.bp;
             if (bp.path != tc.path || bp.tile != tc.tile) continue;
-            if (ga.nseg == kMaxSeg) {
+            const int64_t tm = bp.m_pad / bp.tile, tn = bp.n_pad / bp.tile;
+            const int64_t blocks = (int64_t)bp.members.size() * (phase == kBX ? tm * tn : tm * (tm + 1) / 2);
+            if (ga.nseg == kMaxSeg || (int64_t)ga.total_blocks + blocks > (int64_t)INT32_MAX) {
                 hipError_t e = flush();
                 if (e != hipSuccess) return e;
             }
@@ -126,12 +130,26 @@ int32_t seg_len_for(const BucketPlan& bp, const StepParams& sp) {
     return growth <= 64.0 ? bp.seg_len : 1;
 }
 
+dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
+                      void* const* events);
+
+// The enqueue sequence behind every step entry point; host allocation
+// failures come back as a status, never as an exception across the ABI.
+dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
+                 void* const* events = nullptr) {
+    try {
+        return run_impl(p, sp, workspace, stream, events);
+    } catch (const std::bad_alloc&) {
+        return DMUON_ERR_ALLOC;
+    }
+}
+
 // events == nullptr: plain run.  Otherwise events[0] is recorded before the
 // first launch and events[1 + k] after phase k, phases being: prep (records,
 // momentum/cast, norms), then per iteration Gram, square, prod, BX (each
 // possibly empty), then apply.
-dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
-                 void* const* events = nullptr) {
+dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
+                      void* const* events) {
     const int32_t count = (int32_t)p->mats.size();
     if (count == 0) return DMUON_OK;
     int ev = 0;
@@ -317,7 +335,7 @@ extern "C" dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const v
 }
 
 extern "C" int32_t muon_step_event_count(int32_t ns_steps) {
-    return ns_steps < 0 ? -1 : 3 + 4 * ns_steps;
+    return ns_steps < 0 || ns_steps > (INT32_MAX - 3) / 4 ? -1 : 3 + 4 * ns_steps;
 }
 
 extern "C" dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const void* const* grads,
@@ -326,7 +344,7 @@ extern "C" dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const
                                                    size_t workspace_bytes, void* stream,
                                                    void* const* events, int32_t num_events) {
     if (plan == nullptr || hp == nullptr || hp->ns_steps < 0 || events == nullptr ||
-        num_events < muon_step_event_count(hp->ns_steps))
+        muon_step_event_count(hp->ns_steps) < 0 || num_events < muon_step_event_count(hp->ns_steps))
         return DMUON_ERR_INVALID_ARG;
     for (int32_t i = 0; i < num_events; ++i)
         if (events[i] == nullptr) return DMUON_ERR_INVALID_ARG;

@@ -17,6 +17,7 @@
 // iterations, 5 iterations cost 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3.
 // The bucket ordering keeps the cost above.
 #include <algorithm>
+#include <climits>
 #include <map>
 #include <new>
 #include <tuple>
@@ -39,6 +40,7 @@ int32_t tile_granularity(int32_t path, int64_t m) {
 bool valid_dtype(int32_t d) { return d == DMUON_F32 || d == DMUON_BF16; }
 
 struct InvalidEntry {};  // a tuned entry that applies to a bucket but cannot run it
+struct TooLarge {};      // a bucket whose launch would exceed 32-bit block ids
 
 }  // namespace
 
@@ -144,6 +146,12 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
             if (e->xcd_remap != DMUON_XCD_REMAP_DEFAULT) bp.xcd_mask = e->xcd_remap;
             bp.cost_ms = e->cost_ms_per_matrix;
         }
+        // a bucket's launch must stay within 32-bit block ids (B X has the
+        // most tiles per matrix)
+        for (const auto& bp : tmp) {
+            const int64_t tiles = (bp.m_pad / bp.tile) * (bp.n_pad / bp.tile);
+            if ((int64_t)bp.members.size() * tiles > (int64_t)INT32_MAX) throw TooLarge();
+        }
         // order buckets by executed cost, descending -- measured, when every
         // bucket has a measured cost, else dense; stable sort keeps first
         // appearance on ties
@@ -211,6 +219,9 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
     } catch (const InvalidEntry&) {
         delete p;
         return DMUON_ERR_INVALID_ARG;
+    } catch (const TooLarge&) {
+        delete p;
+        return DMUON_ERR_UNSUPPORTED;
     }
     *out = p;
     return DMUON_OK;

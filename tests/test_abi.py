@@ -39,6 +39,8 @@ def test_event_count():
     assert LIB.muon_step_event_count(5) == 23 and LIB.muon_step_event_count(0) == 3
     assert LIB.muon_step_event_count(1) == 7
     assert LIB.muon_step_event_count(-1) == -1
+    assert LIB.muon_step_event_count((2 ** 31 - 1 - 3) // 4) == 2 ** 31 - 1
+    assert LIB.muon_step_event_count((2 ** 31 - 1 - 3) // 4 + 1) == -1
 
 
 def test_status_strings_and_version():
@@ -223,6 +225,11 @@ def test_plan_errors():
         d.Plan([(5, (1 << 27) + 1, 1, 1)])
     assert e.value.status == d.DMUON_ERR_UNSUPPORTED
     d.Plan([(5, 1 << 27, 1, 1)]).close()
+    # a bucket whose B X launch would exceed 2^31 - 1 tiles (here 4096 x 2^19)
+    with pytest.raises(d.DMuonError) as e:
+        d.Plan([(256, 1 << 27, 1, 1)] * 4096)
+    assert e.value.status == d.DMUON_ERR_UNSUPPORTED
+    d.Plan([(256, 1 << 27, 1, 1)] * 4095).close()
     d.Plan([(5, (1 << 27) + 1, 0, 0)]).close()
     out = ctypes.c_void_p()
     assert LIB.muon_plan(None, 3, ctypes.byref(out)) == d.DMUON_ERR_INVALID_ARG
