@@ -341,3 +341,48 @@ def test_header_is_plain_c():
         r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{inc}", src, "-o",
                             os.path.join(td, "t")], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_c_program_links_and_plans():
+    # a plain C99 program against the shared library: plan, query, workspace,
+    # status strings and argument errors, no Python in between
+    import subprocess
+    import tempfile
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc, libdir = os.path.join(root, "include"), os.path.dirname(d.library_path())
+    prog = r'''
+#include <stdio.h>
+#include "dmuon_ns.h"
+int main(void) {
+    dmuon_matrix_desc descs[3] = {{4096, 14336, DMUON_BF16, DMUON_BF16}, {14336, 4096, DMUON_BF16, DMUON_F32},
+                                  {256, 512, DMUON_F32, DMUON_F32}};
+    dmuon_plan* plan = NULL;
+    if (muon_plan(descs, 3, &plan) != DMUON_OK) return 1;
+    int32_t count = 0, buckets = 0, algo = 0, restart = 0, bucket = -1, slot = -1, tr = -1;
+    size_t ws = 0;
+    int64_t pm = 0, pn = 0, cost = 0;
+    if (muon_plan_info(plan, &count, &buckets) != DMUON_OK || count != 3 || buckets != 2) return 2;
+    if (muon_plan_workspace_bytes(plan, &ws) != DMUON_OK || ws == 0) return 3;
+    if (muon_plan_query(plan, 1, &bucket, &slot, &tr, &pm, &pn, &cost) != DMUON_OK) return 4;
+    if (bucket != 0 || slot != 1 || tr != 1 || pm != 4096 || pn != 14336) return 5;
+    if (muon_plan_bucket_algo(plan, 0, &algo, &restart) != DMUON_OK || algo != DMUON_ALGO_GRAM_SPACE || restart != 3)
+        return 6;
+    if (muon_plan_query(plan, 3, &bucket, NULL, NULL, NULL, NULL, NULL) != DMUON_ERR_INVALID_ARG) return 7;
+    dmuon_hparams hp = {0.02f, 0.95f, 0.0f, 1e-7f, 3.4445f, -4.7750f, 2.0315f, 5, 1};
+    if (muon_step_batched(plan, NULL, NULL, NULL, &hp, NULL, 0, NULL) != DMUON_ERR_INVALID_ARG) return 8;
+    muon_plan_destroy(plan);
+    printf("%s %s\n", dmuon_version(), dmuon_status_string(DMUON_ERR_WORKSPACE));
+    return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as td:
+        src, exe = os.path.join(td, "p.c"), os.path.join(td, "p")
+        with open(src, "w") as f:
+            f.write(prog)
+        r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{inc}", src, f"-L{libdir}", "-ldmuon_ns",
+                            f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+        assert r.stdout.split()[0] == d.version()
