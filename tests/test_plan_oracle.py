@@ -67,3 +67,37 @@ def test_llama8b_owner_share():
     items, buckets = plan_reference([(s.rows, s.cols, BF16, BF16) for s in w.matrices])
     assert [(b["m_pad"], b["n_pad"], len(b["members"])) for b in buckets] == [
         (4096, 14336, 12), (4096, 4096, 8), (1024, 4096, 8)]
+
+
+def test_recurrence_form_by_hand():
+    # (300, 700): m_pad 512 < n_pad 768, 700 >= 1.5*300 -> Gram space (restart 3)
+    # (384, 500): m_pad 512, n_pad 512 -> short side
+    # (200, 290): m_pad 256 < n_pad 512 but 290 < 1.5*200 = 300 -> short side (automatic rule)
+    # (130, 600) f32: always short side
+    descs = [(300, 700, BF16, BF16), (384, 500, BF16, BF16), (200, 290, BF16, BF16), (130, 600, F32, F32)]
+    _, buckets = plan_reference(descs)
+    form = {(b["path"], b["m_pad"], b["n_pad"]): (b["algo"], b["gram_restart"]) for b in buckets}
+    assert form == {("bf16", 512, 768): ("gram_space", 3), ("bf16", 512, 512): ("short_side", 1),
+                    ("bf16", 256, 512): ("short_side", 1), ("f32", 192, 640): ("short_side", 1)}
+    _, forced = plan_reference(descs, "gram_space", 2)
+    assert {(b["path"], b["algo"], b["gram_restart"]) for b in forced} == {
+        ("bf16", "gram_space", 2), ("f32", "short_side", 1)}
+
+
+def test_tuned_entries_by_hand():
+    descs = [(256, 512, BF16, BF16), (1024, 4096, BF16, BF16), (256, 512, BF16, BF16), (128, 128, BF16, BF16)]
+    # dense order without measurements: 1024x4096 (1 x 19327352832), 256x512 (2 x 301989888),
+    # 128x128 (1 x 12582912)
+    _, b0 = plan_reference(descs)
+    assert [(b["m_pad"], b["n_pad"]) for b in b0] == [(1024, 4096), (256, 512), (128, 128)]
+    e = lambda mp, np_, **kw: {"path": BF16, "padded_m": mp, "padded_n": np_, **kw}
+    tuned = [e(256, 512, tile=128, algo=1, xcd_remap=15, cost_ms_per_matrix=3.0),
+             e(1024, 4096, algo=2, gram_restart=2, cost_ms_per_matrix=5.0),
+             e(128, 128, cost_ms_per_matrix=6.0)]
+    # measured order: 256x512 2 x 3.0 = 6.0 ties 128x128 1 x 6.0 (first appearance wins), then 5.0
+    _, b1 = plan_reference(descs, tuned=tuned)
+    assert [(b["m_pad"], b["tile"], b["algo"], b["gram_restart"], b["xcd_remap"]) for b in b1] == [
+        (256, 128, "short_side", 1, 15), (128, 128, "short_side", 1, 4), (1024, 256, "gram_space", 2, 4)]
+    # one bucket without a cost: the dense order stays
+    _, b2 = plan_reference(descs, tuned=tuned[:2])
+    assert [b["m_pad"] for b in b2] == [1024, 256, 128]
