@@ -25,7 +25,10 @@ traffic against the 8 TB/s HBM peak.  ``adamw`` times the AdamW companion
 step on Llama-3.1-8B's non-Muon parameters (one GPU's 1/8 element share) the
 same way.  ``graph`` replays the same step from a HIP graph (no host enqueueing
 in the timed span; the number that matters for small, launch-bound
-workloads).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
+workloads).  ``step_ms_median`` and ``step_ms_min`` are the steps' device
+times from their first to their last event.  ``torch_baseline`` times the same
+step written with PyTorch matrix products (hipBLASLt) on the same inputs, for
+context.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
 the same workload.
 """
 
@@ -149,6 +152,43 @@ def graph_bench(d, plan, G, M, W, ws, reps: int, count: int):
     return {"replays": reps, "ms_per_step": round(ms, 4), "matrices_per_s": round(count / (ms / 1e3), 2)}
 
 
+def torch_baseline(G, M, W, steps: int = 3, warmup: int = 1):
+    """The same step written with PyTorch tensor ops on the same GPU, the way a
+    plain Muon implementation runs it: matrix by matrix, momentum and
+    normalisation as tensor expressions and every Newton-Schulz iteration as
+    three torch.mm products (hipBLASLt) on bf16 operands (fp32 on the fp32
+    path), the full X X^T and A A included.  Timed with events on the current
+    stream.  Context only: no part of the library runs here."""
+    import torch
+
+    a, b, c = 3.4445, -4.7750, 2.0315
+
+    def step():
+        for g, mo, p in zip(G, M, W):
+            r, cols = p.shape
+            mo.mul_(BETA).add_(g.float())
+            u = g.float() + BETA * mo
+            x = u.t() if r > cols else u
+            x = (x / (x.norm() + EPS)).to(g.dtype).contiguous()
+            for _ in range(NS_STEPS):
+                A = torch.mm(x, x.t())
+                B = b * A + c * torch.mm(A, A)
+                x = a * x + torch.mm(B, x)
+            o = x.t() if r > cols else x
+            p.add_(o.to(p.dtype), alpha=-LR * max(1.0, r / cols) ** 0.5)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    e1.synchronize()
+    return {"kind": "torch.mm per matrix (hipBLASLt), same inputs and GPU", "steps": steps,
+            "ms_per_step": round(e0.elapsed_time(e1) / steps, 3)}
+
+
 def adamw_bench(d, dev, steps: int = 10, warmup: int = 2):
     """The AdamW companion step on Llama-3.1-8B's non-Muon share, timed with
     HIP events on the current stream; bytes are the step's required traffic
@@ -182,6 +222,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3.1-8b_owner_1of8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW companion measurement")
+    ap.add_argument("--no-torch-baseline", action="store_true",
+                    help="skip timing the same step written with PyTorch matrix products")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--tuning-cache", default=None, metavar="PATH",
                     help="run the plan with per-shape tuning entries: loaded from PATH for this device, "
@@ -266,6 +308,7 @@ def main(argv=None):
 
     names = events[0].names()
     per = [e.elapsed_ms() for e in events]
+    step_gpu = sorted(sum(p) for p in per)  # first to last event of each step
     avg = {nm: sum(p[j] for p in per) / len(per) for j, nm in enumerate(names)}
     kind_of = lambda nm: re.sub(r"\d+$", "", nm)
     gemm_ms = [p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) in ("gram", "square", "prod", "bx")]
@@ -303,6 +346,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(step_gpu[len(step_gpu) // 2], 4),
+        "step_ms_min": round(step_gpu[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -343,6 +388,10 @@ def main(argv=None):
     out["graph"] = graph_bench(d, plan, G, M, W, ws, max(args.steps, 50 if ms_per_step < 5 else 0), w.count)
     if tuning_info is not None:
         out["tuning"] = tuning_info
+    if not args.no_torch_baseline:
+        tb = torch_baseline(G, M, W)
+        tb["library_speedup"] = round(tb["ms_per_step"] / ms_per_step, 3)
+        out["torch_baseline"] = tb
     if not args.no_adamw:
         out["adamw"] = adamw_bench(d, dev)
     if host_samples:

@@ -1,0 +1,78 @@
+"""Host-side logic of bench.py, on the CPU: the one-GPU guard, the flop
+accounting behind ``value``, ``executed_tflops`` and the roofline, and the
+check that ties a committed counter summary to the kernel source it was taken
+on."""
+
+import hashlib
+import os
+
+import pytest
+
+import bench
+from matrix_optimizer_02_amd.workloads import get_workload
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_owner_share_shapes_and_flop_totals():
+    """The Llama-3.1-8B owner share is 12 matrices of 4096 x 14336 (either
+    orientation), 8 of 4096 x 4096 and 8 of 1024 x 4096 (short side first).
+    Its short-side work over 5 iterations, counted by hand per shape class:
+    Gram triangle m(m+1)n, A A^T triangle m(m+1)m, dense B X 2 m^2 n."""
+    w = get_workload("llama3.1-8b_owner_1of8")
+    shapes = sorted((min(s.rows, s.cols), max(s.rows, s.cols)) for s in w.matrices)
+    assert shapes == sorted([(4096, 14336)] * 12 + [(4096, 4096)] * 8 + [(1024, 4096)] * 8)
+    by_hand = 0
+    for m, n, k in ((4096, 14336, 12), (4096, 4096, 8), (1024, 4096, 8)):
+        by_hand += k * 5 * (m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n)
+    total = sum(bench.NS_STEPS * bench.algorithmic_flops(m, n) for m, n in shapes)
+    assert total == by_hand
+    assert abs(total / 1e12 - 58.98) < 0.01
+    dense = sum(bench.NS_STEPS * bench.dense_flops(m, n) for m, n in shapes)
+    assert abs(dense / 1e12 - 83.24) < 0.01
+
+
+@pytest.mark.parametrize("m,n", [(4096, 14336), (1024, 4096), (128, 512), (96, 96)])
+def test_segment_of_one_counts_the_short_side(m, n):
+    ex = bench.executed_flops(m, n, 1)
+    assert ex["prod"] == 0
+    assert sum(ex.values()) == bench.NS_STEPS * bench.algorithmic_flops(m, n)
+
+
+def test_gram_space_counts_by_hand():
+    """Restart after 3: segments of 3 and 2 iterations.  Per segment one Gram
+    triangle, one square per iteration, three m x m triangles per iteration
+    but the last (P' = Q P, T = A Q, A' = Q T) and one B X."""
+    m, n = 1024, 4096
+    tri_n, tri_m = m * (m + 1) * n, m * (m + 1) * m
+    ex = bench.executed_flops(m, n, 3)
+    assert ex == {"gram": 2 * tri_n, "square": 5 * tri_m, "prod": (3 * 2 + 3 * 1) * tri_m,
+                  "bx": 2 * 2 * m * m * n}
+    # a segment as long as the loop: one Gram, one B X
+    ex5 = bench.executed_flops(m, n, 5)
+    assert ex5["gram"] == tri_n and ex5["bx"] == 2 * m * m * n and ex5["prod"] == 12 * tri_m
+
+
+def test_traffic_summary_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
+    src_dir = tmp_path / "matrix_optimizer_02_amd" / "csrc"
+    src_dir.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    src = src_dir / "k_gemm_bf16.hip"
+    src.write_text("// kernel v1\n")
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "k_traffic.txt").write_text(
+        f"kernel_source_sha256: {sha}\nhbm_bytes_per_launch: 6.25e9\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.read_traffic("k") == 6.25e9
+    src.write_text("// kernel v2\n")  # the kernel changed since the counters were taken
+    assert bench.read_traffic("k") is None
+    assert bench.read_traffic("missing") is None
+
+
+def test_committed_traffic_summary_parses():
+    path = os.path.join(bench.ROOT, "profiles", "bx_gemm_bf16_llama8b_traffic.txt")
+    text = open(path).read()
+    assert "kernel_source_sha256:" in text and "hbm_bytes_per_launch:" in text
