@@ -211,6 +211,40 @@ def test_zero_gradient_and_momentum():
     assert all(torch.count_nonzero(o) == 0 for o in outs)
 
 
+def test_non_finite_inputs_propagate():
+    """Reading: non-finite values are not masked.  A NaN or an Inf in one
+    gradient leaves that matrix's momentum non-finite at that entry only and
+    its W' NaN everywhere, as in the oracle; every other matrix of the batch,
+    and every other momentum entry, is bit for bit what a clean run gives."""
+    shapes = [(256, 768), (768, 256), (200, 72), (128, 128)]
+    w = custom_workload("nonfinite", shapes, "bf16", "bf16")
+    G, M, W = make_inputs(w, "cuda", seed=3)
+    Gc, Mc, Wc = [x.clone() for x in G], [x.clone() for x in M], [x.clone() for x in W]
+    planted = {0: (5, 7, float("nan")), 1: (100, 3, float("inf")), 3: (0, 0, float("-inf"))}
+    for i, (r, c, v) in planted.items():
+        G[i][r, c] = v
+    host = [(f64(G[i]), f64(M[i]), f64(W[i])) for i in range(len(shapes))]
+    plan = d.plan_for(G, [x.dtype for x in W])
+    say("case non-finite gradients muon_step_batched")
+    d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, workspace=d.workspace_for(plan))
+    d.muon_step_batched(plan, Gc, Mc, Wc, lr=LR, beta=BETA, eps=EPS, workspace=d.workspace_for(plan))
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        if i not in planted:
+            assert torch.equal(M[i], Mc[i]) and torch.equal(W[i].view(torch.int16), Wc[i].view(torch.int16))
+            continue
+        r, c, v = planted[i]
+        with np.errstate(invalid="ignore"):  # Inf / Inf in the normalisation
+            ref = oracle.muon_step(*host[i], lr=LR, beta=BETA, eps=EPS)
+        assert np.isnan(ref["W_new"]).all()
+        assert torch.isnan(W[i]).all(), shapes[i]
+        Mi = f64(M[i])
+        assert (np.isnan(Mi[r, c]) and np.isnan(ref["M_new"][r, c])) or Mi[r, c] == ref["M_new"][r, c] == v
+        keep = torch.ones_like(M[i], dtype=torch.bool)
+        keep[r, c] = False
+        assert torch.equal(M[i][keep], Mc[i][keep])
+
+
 def test_rank_one_and_diagonal_inputs():
     # Diagonal input (exact zeros off the diagonal stay exact): per-entry p^5 on
     # both paths at the usual tolerances.

@@ -340,3 +340,25 @@ def test_gram_space_recurrence_matches_definition(shape, steps):
     for _ in range(steps):
         x = A_ * x + B_ * x ** 3 + C_ * x ** 5
     assert np.linalg.norm(got - (u * x) @ vt) <= 1e-11 * max(np.linalg.norm(got), 1.0)
+
+
+def test_non_finite_inputs_propagate():
+    """Reading: non-finite gradients are not masked.  Momentum is elementwise,
+    so only the planted entry of M' is non-finite; the norm is NaN or Inf, so
+    X is NaN in at least one entry, the Gram product spreads it over a row and
+    a column and the square over everything: O and W' are NaN everywhere."""
+    rng = np.random.default_rng(11)
+    for val, shape in ((np.nan, (6, 10)), (np.inf, (10, 6)), (-np.inf, (7, 7))):
+        G = rng.standard_normal(shape)
+        M = rng.standard_normal(shape)
+        W = rng.standard_normal(shape)
+        G[2, 3] = val
+        with np.errstate(invalid="ignore"):  # Inf / Inf in the normalisation
+            out = oracle.muon_step(G, M, W)
+        bad = ~np.isfinite(out["M_new"])
+        assert bad[2, 3] and bad.sum() == 1
+        if np.isnan(val):
+            assert np.isnan(out["M_new"][2, 3])
+        else:
+            assert out["M_new"][2, 3] == val
+        assert np.isnan(out["O"]).all() and np.isnan(out["W_new"]).all()
