@@ -218,7 +218,8 @@ DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t buc
  * restart, remap bits; cost_ms_per_matrix as given to the plan, else 0). */
 DMUON_API dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t bucket, dmuon_tune_entry* out);
 
-/* Workspace muon_autotune needs for these descs and opts (the largest of its trial plans). */
+/* Workspace muon_autotune needs for these descs and opts (the largest of its
+ * trial plans, the whole batch with every bucket in its largest form included). */
 DMUON_API dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* descs, int32_t count,
                                                      const dmuon_plan_opts* opts, size_t* bytes);
 
@@ -230,7 +231,12 @@ DMUON_API dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* de
  * bf16 path tiles 256 (where it divides the padded dims) and 128, remap bits 0,
  * 4 and 15; the short side, and the Gram space with opts' restart where the
  * plan options would allow it (forced forms are kept); fp32 buckets have one
- * candidate.  inputs / outputs: device pointers as for ns_orthogonalize_batched
+ * candidate.  Then, if some bucket picked the Gram space, the whole batch is
+ * timed twice the same way: with the picked entries, and with every Gram-space
+ * entry replaced by its bucket's fastest short-side one.  The faster set is
+ * returned.  The Gram-space buckets add product launches that the other
+ * buckets lack, and in batches of small matrices that latency can cost more
+ * than the Gram space saves.  inputs / outputs: device pointers as for ns_orthogonalize_batched
  * (trial data; outputs are overwritten).  The call blocks until the trials
  * are done.  Errors: INVALID_ARG (also out_capacity below the bucket count),
  * WORKSPACE (below muon_autotune_workspace_bytes), HIP, ALLOC. */

@@ -10,7 +10,8 @@
 // tile, the XCD order of the tile launches and the form of the recurrence.
 //
 // Host code only: each trial is an ordinary ns_orthogonalize_batched call on a
-// plan holding one bucket, timed with HIP events on the caller's stream.
+// plan holding one bucket (or, for the final check of the forms, the whole
+// batch), timed with HIP events on the caller's stream.
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -87,6 +88,45 @@ struct EventPair {
     }
 };
 
+// The arguments every timed trial shares.
+struct Trial {
+    int32_t ns_steps;
+    float a, b, c;
+    int32_t reps;
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+    EventPair* ev;
+};
+
+// Milliseconds per ns_orthogonalize_batched call of the plan built from descs
+// with options o and the given entries: one untimed call, then t.reps timed.
+dmuon_status time_plan(const Trial& t, const dmuon_matrix_desc* descs, int32_t count, const void* const* inputs,
+                       void* const* outputs, const dmuon_plan_opts& o, const dmuon_tune_entry* entries,
+                       int32_t n_entries, double* ms_per_call) {
+    dmuon_plan_opts oc = o;
+    oc.tuned = entries;
+    oc.tuned_count = n_entries;
+    PlanHolder plan;
+    dmuon_status st = muon_plan_ex(descs, count, &oc, &plan.p);
+    if (st != DMUON_OK) return st;
+    const float eps = 1e-7f;
+    auto call = [&]() {
+        return ns_orthogonalize_batched(plan.p, inputs, outputs, t.ns_steps, t.a, t.b, t.c, eps, t.workspace,
+                                        t.workspace_bytes, t.stream);
+    };
+    if ((st = call()) != DMUON_OK) return st;  // warm-up
+    if (hipEventRecord(t.ev->e[0], t.stream) != hipSuccess) return DMUON_ERR_HIP;
+    for (int32_t r = 0; r < t.reps; ++r)
+        if ((st = call()) != DMUON_OK) return st;
+    float ms = 0.f;
+    if (hipEventRecord(t.ev->e[1], t.stream) != hipSuccess || hipEventSynchronize(t.ev->e[1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, t.ev->e[0], t.ev->e[1]) != hipSuccess)
+        return DMUON_ERR_HIP;
+    *ms_per_call = (double)ms / t.reps;
+    return DMUON_OK;
+}
+
 }  // namespace
 
 extern "C" dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* descs, int32_t count,
@@ -98,9 +138,15 @@ extern "C" dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* d
     if (st != DMUON_OK) return st;
     size_t need = base.p->workspace_bytes;
     try {
+        // per bucket, the candidate with the largest workspace: a whole-batch
+        // plan of those bounds every combination (a bucket's padded dims are
+        // fixed, so its share of the workspace depends on its form alone)
+        std::vector<dmuon_tune_entry> largest;
         for (const BucketPlan& bp : base.p->buckets) {
             std::vector<dmuon_matrix_desc> sub;
             for (int32_t i : bp.members) sub.push_back(descs[i]);
+            size_t largest_bytes = 0;
+            dmuon_tune_entry largest_entry{};
             for (const Candidate& c : candidates(bp, o)) {
                 const dmuon_tune_entry e = entry_for(bp, c);
                 dmuon_plan_opts oc = o;
@@ -110,7 +156,21 @@ extern "C" dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* d
                 st = muon_plan_ex(sub.data(), (int32_t)sub.size(), &oc, &trial.p);
                 if (st != DMUON_OK) return st;
                 need = std::max(need, trial.p->workspace_bytes);
+                if (trial.p->workspace_bytes >= largest_bytes) {
+                    largest_bytes = trial.p->workspace_bytes;
+                    largest_entry = e;
+                }
             }
+            largest.push_back(largest_entry);
+        }
+        if (!largest.empty()) {
+            dmuon_plan_opts oc = o;
+            oc.tuned = largest.data();
+            oc.tuned_count = (int32_t)largest.size();
+            PlanHolder whole;
+            st = muon_plan_ex(descs, count, &oc, &whole.p);
+            if (st != DMUON_OK) return st;
+            need = std::max(need, whole.p->workspace_bytes);
         }
     } catch (const std::bad_alloc&) {
         return DMUON_ERR_ALLOC;
@@ -142,8 +202,10 @@ extern "C" dmuon_status muon_autotune(const dmuon_matrix_desc* descs, int32_t co
     EventPair ev;
     if (nb > 0 && (hipEventCreate(&ev.e[0]) != hipSuccess || hipEventCreate(&ev.e[1]) != hipSuccess))
         return DMUON_ERR_HIP;
-    const float eps = 1e-7f;
+    const Trial t{ns_steps, a, b, c, reps, workspace, workspace_bytes, s, &ev};
     try {
+        std::vector<dmuon_tune_entry> best_short(nb);
+        std::vector<char> has_short(nb, 0);
         for (int32_t bi = 0; bi < nb; ++bi) {
             const BucketPlan& bp = base.p->buckets[bi];
             std::vector<dmuon_matrix_desc> sub;
@@ -154,36 +216,46 @@ extern "C" dmuon_status muon_autotune(const dmuon_matrix_desc* descs, int32_t co
                 in.push_back(inputs[i]);
                 outp.push_back(outputs[i]);
             }
-            double best_ms = -1.0;
+            const double per_matrix = 1.0 / (double)bp.members.size();
+            double best_ms = -1.0, short_ms = -1.0;
             dmuon_tune_entry best{};
             for (const Candidate& cand : candidates(bp, o)) {
                 dmuon_tune_entry e = entry_for(bp, cand);
-                dmuon_plan_opts oc = o;
-                oc.tuned = &e;
-                oc.tuned_count = 1;
-                PlanHolder trial;
-                st = muon_plan_ex(sub.data(), (int32_t)sub.size(), &oc, &trial.p);
+                double ms = 0.0;
+                st = time_plan(t, sub.data(), (int32_t)sub.size(), in.data(), outp.data(), o, &e, 1, &ms);
                 if (st != DMUON_OK) return st;
-                auto call = [&]() {
-                    return ns_orthogonalize_batched(trial.p, in.data(), outp.data(), ns_steps, a, b, c, eps, workspace,
-                                                    workspace_bytes, stream);
-                };
-                if ((st = call()) != DMUON_OK) return st;  // warm-up
-                if (hipEventRecord(ev.e[0], s) != hipSuccess) return DMUON_ERR_HIP;
-                for (int32_t r = 0; r < reps; ++r)
-                    if ((st = call()) != DMUON_OK) return st;
-                float ms = 0.f;
-                if (hipEventRecord(ev.e[1], s) != hipSuccess || hipEventSynchronize(ev.e[1]) != hipSuccess ||
-                    hipEventElapsedTime(&ms, ev.e[0], ev.e[1]) != hipSuccess)
-                    return DMUON_ERR_HIP;
-                const double per_call = (double)ms / reps;
-                if (best_ms < 0.0 || per_call < best_ms) {
-                    best_ms = per_call;
+                e.cost_ms_per_matrix = ms * per_matrix;
+                if (best_ms < 0.0 || ms < best_ms) {
+                    best_ms = ms;
                     best = e;
                 }
+                if (cand.algo == DMUON_ALGO_SHORT_SIDE && (short_ms < 0.0 || ms < short_ms)) {
+                    short_ms = ms;
+                    best_short[bi] = e;
+                    has_short[bi] = 1;
+                }
             }
-            best.cost_ms_per_matrix = best_ms / (double)bp.members.size();
             out[bi] = best;
+        }
+        // The Gram-space buckets of a batch add product launches that the other
+        // buckets do not have; with small matrices their latency can outweigh
+        // what the Gram space saves, which no bucket timed alone shows.  So the
+        // whole batch is timed with the chosen entries and with every
+        // Gram-space entry replaced by its bucket's fastest short-side one, and
+        // the faster set is kept.
+        std::vector<dmuon_tune_entry> alt(out, out + nb);
+        bool differs = false;
+        for (int32_t bi = 0; bi < nb; ++bi)
+            if (out[bi].algo == DMUON_ALGO_GRAM_SPACE && has_short[bi]) {
+                alt[bi] = best_short[bi];
+                differs = true;
+            }
+        if (differs) {
+            double chosen_ms = 0.0, alt_ms = 0.0;
+            if ((st = time_plan(t, descs, count, inputs, outputs, o, out, nb, &chosen_ms)) != DMUON_OK ||
+                (st = time_plan(t, descs, count, inputs, outputs, o, alt.data(), nb, &alt_ms)) != DMUON_OK)
+                return st;
+            if (alt_ms < chosen_ms) std::copy(alt.begin(), alt.end(), out);
         }
     } catch (const std::bad_alloc&) {
         return DMUON_ERR_ALLOC;

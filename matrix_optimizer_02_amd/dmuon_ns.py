@@ -366,8 +366,10 @@ def autotune(inputs: Sequence[torch.Tensor], out_dtypes: Optional[Sequence] = No
              gram_restart: int = 0, ns_steps: int = 5, a: float = 3.4445, b: float = -4.7750,
              c: float = 2.0315, reps: int = 3, stream=None) -> List[TuneEntry]:
     """muon_autotune on these inputs (trial data, read only): one entry per
-    bucket of the plan they form, the fastest measured configuration.  Output
-    buffers and the workspace are allocated here for the trials.  Blocks."""
+    bucket of the plan they form, the fastest measured configuration, with the
+    Gram-space choices checked on the whole batch against the short side.
+    Output buffers and the workspace are allocated here for the trials.
+    Blocks."""
     out_dtypes = out_dtypes or [torch.float32] * len(inputs)
     descs = [(int(x.shape[0]), int(x.shape[1]), _code(x.dtype), _code(od)) for x, od in zip(inputs, out_dtypes)]
     for i, x in enumerate(inputs):

@@ -184,6 +184,14 @@ def test_autotune_argument_errors():
     assert LIB.muon_autotune_workspace_bytes(arr, 1, None, ctypes.byref(need)) == d.DMUON_OK
     # the trial plans include the Gram-space one, whose workspace is the largest
     assert need.value >= d.Plan([(256, 512, 1, 1)], "gram_space").workspace_bytes()
+    # several buckets: the final whole-batch trials run every bucket at once
+    multi = [(128, 128, 1, 1)] * 3 + [(128, 512, 1, 1)] * 4 + [(768, 256, 1, 1)] * 2 + [(96, 160, 0, 0)]
+    marr = (d.MatrixDesc * len(multi))(*[d.MatrixDesc(*x) for x in multi])
+    for algo in ("auto", "gram_space", "short_side"):
+        opts = d._plan_opts(algo, 0, None)
+        assert LIB.muon_autotune_workspace_bytes(marr, len(multi), ctypes.byref(opts),
+                                                 ctypes.byref(need)) == d.DMUON_OK
+        assert need.value >= d.Plan(multi, algo).workspace_bytes()
     got = ctypes.c_int32()
     res = (d.TuneEntry * 1)()
     for reps, cap in ((0, 1), (1, 0)):

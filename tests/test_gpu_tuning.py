@@ -117,3 +117,26 @@ def test_autotune_entries_and_parity(tmp_path):
     for i, x in enumerate(xs):
         e = rel(f64(outs[i]), oracle.newton_schulz(f64(x), 5, A, B, C, EPS))
         assert e < TOL, (SHAPES[i], e)
+
+
+def test_autotune_mixed_small_batch():
+    """A batch of small square and wide matrices (the 96-matrix small-batch
+    shapes at a third of the count): the entries are valid whichever form the
+    whole-batch check keeps, square buckets stay on the short side, and a plan
+    from them meets the bar."""
+    shapes = [(128, 128)] * 11 + [(128, 512)] * 11 + [(512, 128)] * 11
+    w = custom_workload("tuning_small", shapes, "bf16", "bf16", g_std=1.0)
+    xs = [host_tensor(w, i, GRAD, seed=6).cuda() for i in range(w.count)]
+    say("case muon_autotune on a mixed small batch, reps 2")
+    ents = d.autotune(xs, reps=2)
+    assert len(ents) == d.plan_for(xs, [torch.float32] * len(xs)).info()[1]
+    for e in ents:
+        say(f"  {e}")
+        assert e.cost_ms_per_matrix > 0 and e.tile == 128
+        if e.padded_m == e.padded_n:
+            assert e.algo == d.ALGO_SHORT_SIDE
+    plan = d.plan_for(xs, [torch.float32] * len(xs), tuning=ents)
+    outs = orth(plan, xs)
+    for i, x in enumerate(xs):
+        e = rel(f64(outs[i]), oracle.newton_schulz(f64(x), 5, A, B, C, EPS))
+        assert e < TOL, (shapes[i], e)
