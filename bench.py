@@ -65,13 +65,17 @@ def bx_flops(m: int, n: int) -> int:
     return 2 * m * m * n
 
 
-def executed_flops(m: int, n: int, seg_len: int, steps: int = NS_STEPS) -> dict:
+def executed_flops(m: int, n: int, seg_len: int, steps: int = NS_STEPS, resident: bool = False) -> dict:
     """Flops one matrix's iterations perform, per phase kind, on the real
     shape with triangles halved as the kernels compute them.  The iterations
     run as segments of seg_len (1: the short side; the last segment shorter);
     a segment of L iterations takes one Gram product, L squares, 3 (L - 1)
-    m x m triangles (P' = Q P, T = A Q, A' = Q T) and one B X product."""
+    m x m triangles (P' = Q P, T = A Q, A' = Q T) and one B X product.  A
+    resident bucket (every iteration in one workgroup) computes X X^T and A A
+    whole."""
     tri_n, tri_m = m * (m + 1) * n, m * (m + 1) * m
+    if resident:
+        tri_n, tri_m = 2 * m * m * n, 2 * m * m * m
     segs = [seg_len] * (steps // seg_len) + ([steps % seg_len] if steps % seg_len else [])
     out = {"gram": 0, "square": 0, "prod": 0, "bx": 0}
     for L in segs:
@@ -316,13 +320,14 @@ def main(argv=None):
     # the recurrence form the plan picked for each matrix's bucket (iterations per segment)
     seg_len = [plan.bucket(plan.query(i).bucket).gram_restart for i in range(w.count)]
     gram_space = [plan.bucket(plan.query(i).bucket).algo == d.ALGO_GRAM_SPACE for i in range(w.count)]
+    resident = [plan.bucket(plan.query(i).bucket).resident for i in range(w.count)]
     alg = dense = 0
     execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}
-    for s, L in zip(w.matrices, seg_len):
+    for s, L, res in zip(w.matrices, seg_len, resident):
         m, n = min(s.rows, s.cols), max(s.rows, s.cols)
         alg += NS_STEPS * algorithmic_flops(m, n)
         dense += NS_STEPS * dense_flops(m, n)
-        for k, v in executed_flops(m, n, L).items():
+        for k, v in executed_flops(m, n, L, resident=res).items():
             execd[k] += v
     executed = sum(execd.values())
     step_s = ms_per_step / 1e3
@@ -359,6 +364,7 @@ def main(argv=None):
         "pct_bf16_peak": round(100.0 * executed / step_s / 1e12 / BF16_PEAK_TFLOPS, 3),
         "ns_tflops_dense_equiv": round(dense / step_s / 1e12, 3),
         "recurrence": {"gram_space_matrices": sum(gram_space), "short_side_matrices": w.count - sum(gram_space),
+                       "resident_matrices": sum(resident),
                        "gram_restart": max(seg_len) if any(gram_space) else None},
         "gemm_phases": {k: {"ms": round(phase_tot[k], 4), "executed_flops": execd[k],
                             "tflops": round(execd[k] / (phase_tot[k] / 1e3) / 1e12, 1) if phase_tot[k] > 0 else None}

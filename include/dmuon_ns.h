@@ -142,7 +142,8 @@ typedef struct {
 typedef struct {
     int32_t algo;         /* dmuon_algo; DMUON_ALGO_AUTO (the default) picks the Gram space for
                              bf16 buckets with padded n > padded m whose members all have
-                             n >= 1.5 m, else the short side;
+                             n >= 1.5 m, except resident ones (padded m 128, padded n <= 512:
+                             see muon_plan_bucket_resident), else the short side;
                              DMUON_ALGO_GRAM_SPACE forces it on every bf16 bucket;
                              DMUON_ALGO_SHORT_SIDE forces the short side everywhere.  fp32
                              buckets always run the short side. */
@@ -213,6 +214,14 @@ DMUON_API dmuon_status muon_plan_bucket(const dmuon_plan* plan, int32_t bucket, 
  * Either pointer may be NULL. */
 DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bucket, int32_t* algo,
                                              int32_t* gram_restart);
+
+/* Whether a bucket runs resident: every short-side iteration of each of its
+ * matrices in one workgroup, with the matrix held in LDS, one launch for all
+ * such buckets of a call (1), or as grouped tiled launches per phase (0).
+ * Resident buckets are the bf16 buckets of padded short side 128 and padded
+ * long side at most 512 that run the short side; their product launches would
+ * be latency-bound.  Same arithmetic and roundings either way. */
+DMUON_API dmuon_status muon_plan_bucket_resident(const dmuon_plan* plan, int32_t bucket, int32_t* resident);
 
 /* The configuration a bucket runs with, as a tuning entry (key, tile, algo,
  * restart, remap bits; cost_ms_per_matrix as given to the plan, else 0). */

@@ -166,6 +166,16 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     const size_t nb = p->buckets.size();
     std::vector<int32_t> seg(nb);
     for (size_t b = 0; b < nb; ++b) seg[b] = seg_len_for(p->buckets[b], sp);
+    // small short-side buckets whose iterations run in one launch, in LDS
+    std::vector<char> resident(nb, 0);
+    std::vector<ResidentBucket> resident_list;
+    for (size_t b = 0; b < nb; ++b) {
+        const BucketPlan& bp = p->buckets[b];
+        if (steps > 0 && bp.algo == DMUON_ALGO_SHORT_SIDE && resident_shape(bp.path, bp.m_pad, bp.n_pad)) {
+            resident[b] = 1;
+            resident_list.push_back({bp.plan_base, (int32_t)bp.members.size(), bp.n_pad});
+        }
+    }
 
     // per-matrix records, plan order, written into the workspace by small launches
     RecChunk chunk{};
@@ -220,6 +230,10 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     if (launch_finalize_norms(table, count, partials, scale, sp.eps, stream) != hipSuccess)
         return DMUON_ERR_HIP;
     if (!mark()) return DMUON_ERR_HIP;
+    // the resident buckets' whole iteration (timed with iteration 0's Gram phase)
+    if (!resident_list.empty() &&
+        launch_resident(table, ws, scale, sp.a, sp.b, sp.c, steps, resident_list, stream) != hipSuccess)
+        return DMUON_ERR_HIP;
 
     // The iterations as segments of seg[b] iterations per bucket (1: the
     // short side).  Iteration k is position j = k mod L of its segment, whose
@@ -254,24 +268,28 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
             lc[b] = std::min(seg[b], steps - (it - j[b]));
         }
         for (size_t b = 0; b < nb; ++b)
-            if (j[b] == 0) segs.push_back({&p->buckets[b], xoff(b, xcur[b]), 0, roles[b].a, it == 0 ? 1 : 0});
+            if (!resident[b] && j[b] == 0)
+                segs.push_back({&p->buckets[b], xoff(b, xcur[b]), 0, roles[b].a, it == 0 ? 1 : 0});
         if (!phase_done(kGram) || !mark()) return DMUON_ERR_HIP;
 
-        for (size_t b = 0; b < nb; ++b) segs.push_back({&p->buckets[b], roles[b].a, 0, roles[b].q, 0});
+        for (size_t b = 0; b < nb; ++b)
+            if (!resident[b]) segs.push_back({&p->buckets[b], roles[b].a, 0, roles[b].q, 0});
         if (!phase_done(kSquare) || !mark()) return DMUON_ERR_HIP;
 
         for (size_t b = 0; b < nb; ++b) {
             const Roles& r = roles[b];
+            if (resident[b]) continue;
             if (j[b] >= 1) segs.push_back({&p->buckets[b], r.q, r.p, r.p2, 0});
             if (j[b] < lc[b] - 1) segs.push_back({&p->buckets[b], r.a, r.q, r.t, 0});
         }
         if (!phase_done(kProd)) return DMUON_ERR_HIP;
         for (size_t b = 0; b < nb; ++b)
-            if (j[b] < lc[b] - 1) segs.push_back({&p->buckets[b], roles[b].q, roles[b].t, roles[b].a, 0});
+            if (!resident[b] && j[b] < lc[b] - 1)
+                segs.push_back({&p->buckets[b], roles[b].q, roles[b].t, roles[b].a, 0});
         if (!phase_done(kProd) || !mark()) return DMUON_ERR_HIP;
 
         for (size_t b = 0; b < nb; ++b) {
-            if (j[b] != lc[b] - 1) continue;
+            if (resident[b] || j[b] != lc[b] - 1) continue;
             const int64_t pfin = j[b] == 0 ? roles[b].q : roles[b].p2;  // P_Lc
             segs.push_back({&p->buckets[b], xoff(b, xcur[b]), pfin, xoff(b, 1 - xcur[b]), it == j[b] ? 1 : 0});
         }

@@ -24,6 +24,14 @@ constexpr int32_t kDefaultGramRestart = 3;
 // XCD's L2.
 constexpr uint32_t kDefaultXcdMask = 1u << 2;
 constexpr uint32_t kAllPhasesMask = 0xFu;
+// Buckets small enough to run every iteration in one workgroup with X in LDS
+// (k_resident.hip): bf16 path, padded short side 128, padded long side at
+// most 512, short-side iterations.
+constexpr int64_t kResidentM = 128;
+constexpr int64_t kResidentMaxN = 512;
+inline bool resident_shape(int path, int64_t m_pad, int64_t n_pad) {
+    return path == kPathBF16 && m_pad == kResidentM && n_pad >= kResidentM && n_pad <= kResidentMaxN;
+}
 // Longest side a bf16-gradient matrix may have: the bf16 kernels address up
 // to 8 rows of a slab with one 32-bit byte offset per lane.
 constexpr int64_t kMaxBf16Side = int64_t(1) << 27;

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "dmuon_internal.h"
 
 namespace dmuon {
@@ -118,5 +120,18 @@ struct AdamArgs {
 };
 
 hipError_t launch_adamw(const AdamArgs& a, hipStream_t stream);
+
+// ---- small matrices resident in LDS (k_resident.hip) ---------------------------
+
+struct ResidentBucket {
+    int32_t plan_base;  // first plan index of the bucket's matrices
+    int32_t count;
+    int64_t n_pad;
+};
+
+// All ns_steps (> 0) iterations of the given buckets' matrices: X from each
+// record's copy 0, the result into its copy final_copy.
+hipError_t launch_resident(const DevMatRec* recs, char* ws, const float* scale, float a, float b, float c,
+                           int32_t steps, const std::vector<ResidentBucket>& buckets, hipStream_t stream);
 
 }  // namespace dmuon

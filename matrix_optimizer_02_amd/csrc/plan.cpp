@@ -110,12 +110,14 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
         // side exceeds the padded short one; by default it is also kept off
         // buckets holding a matrix whose real long side is under 1.5 times its
         // short side (a near-square matrix has small singular values, which the
-        // Gram space resolves worse, and there it saves little).  fp32 buckets
-        // keep the short side.
+        // Gram space resolves worse, and there it saves little), and off the
+        // buckets small enough to run all their iterations in one launch on the
+        // short side (their launches, not their flops, set their time).  fp32
+        // buckets keep the short side.
         for (auto& bp : tmp) {
             bool gram = bp.path == kPathBF16 && algo_opt != DMUON_ALGO_SHORT_SIDE;
             if (gram && algo_opt == DMUON_ALGO_AUTO) {
-                gram = bp.n_pad > bp.m_pad;
+                gram = bp.n_pad > bp.m_pad && !resident_shape(bp.path, bp.m_pad, bp.n_pad);
                 for (int32_t i : bp.members) gram = gram && 2 * p->mats[i].n >= 3 * p->mats[i].m;
             }
             bp.algo = gram ? DMUON_ALGO_GRAM_SPACE : DMUON_ALGO_SHORT_SIDE;
@@ -277,6 +279,14 @@ extern "C" dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t bu
     if (plan == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size()) return DMUON_ERR_INVALID_ARG;
     if (algo) *algo = plan->buckets[bucket].algo;
     if (gram_restart) *gram_restart = plan->buckets[bucket].seg_len;
+    return DMUON_OK;
+}
+
+extern "C" dmuon_status muon_plan_bucket_resident(const dmuon_plan* plan, int32_t bucket, int32_t* resident) {
+    if (plan == nullptr || resident == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size())
+        return DMUON_ERR_INVALID_ARG;
+    const BucketPlan& bp = plan->buckets[bucket];
+    *resident = bp.algo == DMUON_ALGO_SHORT_SIDE && resident_shape(bp.path, bp.m_pad, bp.n_pad) ? 1 : 0;
     return DMUON_OK;
 }
 

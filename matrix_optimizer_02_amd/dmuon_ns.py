@@ -101,6 +101,7 @@ def _load():
         "muon_plan": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, vpp]),
         "muon_plan_ex": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts), vpp]),
         "muon_plan_bucket_algo": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p]),
+        "muon_plan_bucket_resident": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p]),
         "muon_plan_bucket_config": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(TuneEntry)]),
         "muon_autotune_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32,
                                                          ctypes.POINTER(PlanOpts), ctypes.POINTER(ctypes.c_size_t)]),
@@ -180,6 +181,7 @@ class BucketEntry:
     tile: int
     algo: int          # ALGO_SHORT_SIDE | ALGO_GRAM_SPACE
     gram_restart: int  # iterations per Gram-space segment (1 on the short side)
+    resident: bool     # every iteration in one workgroup per matrix, in LDS
 
 
 class Plan:
@@ -233,7 +235,10 @@ class Plan:
         algo, restart = ctypes.c_int32(), ctypes.c_int32()
         _check(_lib.muon_plan_bucket_algo(self._h, int(b), ctypes.byref(algo), ctypes.byref(restart)),
                "muon_plan_bucket_algo")
-        return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value)
+        res = ctypes.c_int32()
+        _check(_lib.muon_plan_bucket_resident(self._h, int(b), ctypes.byref(res)), "muon_plan_bucket_resident")
+        return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value,
+                           bool(res.value))
 
     def config(self, b: int) -> TuneEntry:
         """The configuration bucket b runs with, as a tuning entry."""

@@ -68,6 +68,8 @@ def bucket_algo(path: str, m_pad: int, n_pad: int, shapes, option: str = "auto")
         return "short_side"
     if option == "gram_space":
         return "gram_space"
+    if m_pad == 128 and n_pad <= 512:  # small enough to run every iteration in one launch
+        return "short_side"
     if n_pad > m_pad and all(n >= 1.5 * m for m, n in shapes):
         return "gram_space"
     return "short_side"

@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol():
     names = build_mod.exported_symbols()
     assert set(names) == {"muon_plan", "muon_plan_ex", "muon_plan_workspace_bytes", "muon_plan_info",
                           "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_bucket_config",
+                          "muon_plan_bucket_resident",
                           "muon_autotune_workspace_bytes", "muon_autotune", "muon_plan_destroy",
                           "muon_step_batched",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
@@ -87,17 +88,38 @@ def test_plan_matches_reference(name, algo, restart):
 
 def test_default_algo_by_hand():
     # bf16: Gram space exactly when the padded long side exceeds the padded short side
-    # whose members all have n >= 1.5 m
+    # whose members all have n >= 1.5 m, except for buckets of padded short side 128
+    # and padded long side <= 512 (every iteration in one launch, on the short side)
     p = d.Plan([(4096, 14336, 1, 1), (4096, 4096, 1, 1), (1024, 4096, 0, 0), (200, 256, 1, 1),
-                (128, 192, 1, 1), (100, 250, 1, 1), (384, 1000, 1, 1), (300, 1000, 1, 1)])
+                (128, 192, 1, 1), (100, 250, 1, 1), (384, 1000, 1, 1), (300, 1000, 1, 1),
+                (100, 700, 1, 1), (512, 120, 1, 1)])
     got = {(p.bucket(b).padded_m, p.bucket(b).padded_n, p.bucket(b).path): p.bucket(b).algo
            for b in range(p.info()[1])}
     assert got == {(4096, 14336, 1): d.ALGO_GRAM_SPACE, (4096, 4096, 1): d.ALGO_SHORT_SIDE,
                    (1024, 4096, 0): d.ALGO_SHORT_SIDE, (256, 256, 1): d.ALGO_SHORT_SIDE,
-                   (128, 256, 1): d.ALGO_GRAM_SPACE, (512, 1024, 1): d.ALGO_GRAM_SPACE}
+                   (128, 256, 1): d.ALGO_SHORT_SIDE, (512, 1024, 1): d.ALGO_GRAM_SPACE,
+                   (128, 768, 1): d.ALGO_GRAM_SPACE, (128, 512, 1): d.ALGO_SHORT_SIDE}
     # one near-square member keeps its whole bucket on the short side
     p = d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)])
     assert p.info()[1] == 1 and p.bucket(0).algo == d.ALGO_SHORT_SIDE
+
+
+def test_resident_buckets_by_hand():
+    # bf16, padded short side 128, padded long side <= 512, on the short side
+    descs = [(128, 128, 1, 1), (100, 250, 1, 1), (512, 120, 1, 0), (128, 513, 1, 1), (129, 300, 1, 1),
+             (96, 160, 0, 0), (64, 64, 1, 1)]
+    p = d.Plan(descs)
+    got = {(p.bucket(b).padded_m, p.bucket(b).padded_n, p.bucket(b).path): p.bucket(b).resident
+           for b in range(p.info()[1])}
+    assert got == {(128, 128, 1): True, (128, 256, 1): True, (128, 512, 1): True, (128, 640, 1): False,
+                   (256, 512, 1): False, (128, 192, 0): False}
+    # forced onto every bf16 bucket, the Gram space leaves none resident
+    g = d.Plan(descs, "gram_space")
+    assert not any(g.bucket(b).resident for b in range(g.info()[1]))
+    res = ctypes.c_int32()
+    assert LIB.muon_plan_bucket_resident(None, 0, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_bucket_resident(p.handle, 99, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_bucket_resident(p.handle, 0, None) == d.DMUON_ERR_INVALID_ARG
     assert d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)], "gram_space").bucket(0).algo == d.ALGO_GRAM_SPACE
 
 

@@ -76,3 +76,9 @@ def test_committed_traffic_summary_parses():
     path = os.path.join(bench.ROOT, "profiles", "bx_gemm_bf16_llama8b_traffic.txt")
     text = open(path).read()
     assert "kernel_source_sha256:" in text and "hbm_bytes_per_launch:" in text
+
+
+def test_resident_counts_whole_products():
+    m, n = 100, 400
+    ex = bench.executed_flops(m, n, 1, resident=True)
+    assert ex == {"gram": 5 * 2 * m * m * n, "square": 5 * 2 * m ** 3, "prod": 0, "bx": 5 * 2 * m * m * n}

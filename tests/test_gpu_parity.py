@@ -158,6 +158,26 @@ def test_orthogonalize_shapes(name, ns_steps, algo):
         assert rel(f64(outs[i]), ref) < TOL[dt], (shapes[i], rel(f64(outs[i]), ref))
 
 
+# every padded long side the resident kernel takes (128 .. 512), wide, tall, square,
+# ragged and single-row
+RESIDENT_SHAPES = [(128, 128), (100, 250), (77, 300), (120, 512), (512, 128), (300, 77), (1, 200), (64, 64),
+                   (128, 384), (37, 129)]
+
+
+@pytest.mark.parametrize("ns_steps", [1, 2, 5])
+def test_resident_buckets(ns_steps):
+    w = custom_workload("resident", RESIDENT_SHAPES, "bf16", "bf16", g_std=1.0)
+    Gs = [host_tensor(w, i, GRAD, seed=12) for i in range(w.count)]
+    dev = [g.cuda() for g in Gs]
+    plan = d.plan_for(dev, [torch.float32] * len(dev))
+    assert all(plan.bucket(b).resident for b in range(plan.info()[1]))
+    say(f"case resident buckets ns_orthogonalize_batched ns_steps={ns_steps}")
+    outs = orth_gpu(dev, ns_steps=ns_steps)
+    for i, g in enumerate(Gs):
+        ref = oracle.newton_schulz(f64(g), ns_steps, A, B, C, EPS)
+        assert rel(f64(outs[i]), ref) < TOL["bf16"], (RESIDENT_SHAPES[i], rel(f64(outs[i]), ref))
+
+
 @pytest.mark.parametrize("name", sorted(SHAPE_SETS))
 def test_step_shapes(name):
     shapes, dt = SHAPE_SETS[name]
