@@ -25,6 +25,12 @@
 #include "kcommon.h"
 #include "launch.h"
 
+#ifndef DMUON_RES_UNROLL
+#define DMUON_RES_UNROLL 1
+#endif
+#define DMUON_PRAGMA_(x) _Pragma(#x)
+#define DMUON_PRAGMA(x) DMUON_PRAGMA_(x)
+
 namespace dmuon {
 namespace {
 
@@ -72,14 +78,24 @@ __device__ __forceinline__ void sym_product(const char* P, int row_bytes, int K,
     for (int j = 0; j < 2; ++j)
         #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-    for (int k = 0; k < K; k += 16) {
+    // the next k-step's fragments are read before this one's MFMAs
+    bf16x8 fa = ld8(P, loff(ra, 8 * khalf, row_bytes));
+    bf16x8 fb0 = ld8(P, loff(rb0, 8 * khalf, row_bytes));
+    bf16x8 fb1 = ld8(P, loff(rb0 + 32, 8 * khalf, row_bytes));
+    DMUON_PRAGMA(unroll DMUON_RES_UNROLL)
+    for (int k = 16; k < K; k += 16) {
         const int c = k + 8 * khalf;
-        const bf16x8 fa = ld8(P, loff(ra, c, row_bytes));
-        const bf16x8 fb0 = ld8(P, loff(rb0, c, row_bytes));
-        const bf16x8 fb1 = ld8(P, loff(rb0 + 32, c, row_bytes));
+        const bf16x8 na = ld8(P, loff(ra, c, row_bytes));
+        const bf16x8 nb0 = ld8(P, loff(rb0, c, row_bytes));
+        const bf16x8 nb1 = ld8(P, loff(rb0 + 32, c, row_bytes));
         acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc[1], 0, 0, 0);
+        fa = na;
+        fb0 = nb0;
+        fb1 = nb1;
     }
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb0, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb1, acc[1], 0, 0, 0);
 }
 
 struct ResidentSeg {
@@ -192,7 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs a
             for (int ib = 0; ib < 4; ++ib)
                 #pragma unroll
                 for (int v = 0; v < 16; ++v) bx[ib][v] = 0.f;
-            for (int k = 0; k < kM; k += 16) {
+            // fragments of k-step k: X (transposing reads) and the four B' rows
+            auto frag = [&](int k, bf16x8& fa, bf16x8 (&fb)[4]) {
                 shortx4 h[2];
                 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -201,12 +218,22 @@ __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs a
                     h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_shortx4*)((__attribute__((address_space(3))) char*)X + loff(row, col, xrow)));
                 }
-                const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                const int kc = k + 8 * khalf;
+                fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    const bf16x8 fb = ld8(Ar, loff(32 * ib + lrow, kc, kARowBytes));
-                    bx[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, bx[ib], 0, 0, 0);
+                for (int ib = 0; ib < 4; ++ib) fb[ib] = ld8(Ar, loff(32 * ib + lrow, k + 8 * khalf, kARowBytes));
+            };
+            bf16x8 fa, fb[4];
+            frag(0, fa, fb);
+            #pragma unroll
+            for (int k = 16; k <= kM; k += 16) {
+                bf16x8 na, nb[4];
+                if (k < kM) frag(k, na, nb);
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) bx[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[ib], bx[ib], 0, 0, 0);
+                if (k < kM) {
+                    fa = na;
+                    #pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) fb[ib] = nb[ib];
                 }
             }
             // this wave alone reads and writes columns rb .. rb + 31 of X
