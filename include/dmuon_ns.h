@@ -239,8 +239,8 @@ DMUON_API dmuon_status muon_autotune_workspace_bytes(const dmuon_matrix_desc* de
  * then reps (>= 1) calls timed with HIP events on `stream`.  Candidates: on the
  * bf16 path tiles 256 (where it divides the padded dims) and 128, remap bits 0,
  * 4 and 15; the short side, and the Gram space with opts' restart where the
- * plan options would allow it (forced forms are kept); fp32 buckets have one
- * candidate.  Then, if some bucket picked the Gram space, the whole batch is
+ * plan options would allow it (forced forms are kept); fp32 buckets and
+ * resident ones (muon_plan_bucket_resident) have one candidate.  Then, if some bucket picked the Gram space, the whole batch is
  * timed twice the same way: with the picked entries, and with every Gram-space
  * entry replaced by its bucket's fastest short-side one.  The faster set is
  * returned.  The Gram-space buckets add product launches that the other

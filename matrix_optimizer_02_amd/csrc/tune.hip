@@ -45,6 +45,11 @@ std::vector<Candidate> candidates(const BucketPlan& bp, const dmuon_plan_opts& o
         out.push_back({bp.tile, DMUON_ALGO_SHORT_SIDE, kDefaultXcdMask});
         return out;
     }
+    // a resident bucket has nothing to vary: one workgroup per matrix, in LDS
+    if (bp.algo == DMUON_ALGO_SHORT_SIDE && resident_shape(bp.path, bp.m_pad, bp.n_pad)) {
+        out.push_back({bp.tile, DMUON_ALGO_SHORT_SIDE, kDefaultXcdMask});
+        return out;
+    }
     std::vector<int32_t> tiles;
     if (bp.m_pad % 256 == 0 && bp.n_pad % 256 == 0) tiles.push_back(256);
     tiles.push_back(128);
