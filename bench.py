@@ -15,8 +15,8 @@ B X product), divided by the step time -- a fixed amount of work per workload,
 so ``value`` moves with 1 / step time whichever form of the recurrence runs.
 ``executed_tflops`` and ``pct_bf16_peak`` count the flops the library actually
 performs (fewer for buckets that run the Gram-space form: 6 m^2 n + 14 m^3
-over 5 iterations with a restart after 3, triangles halved), i.e. the
-matrix-core utilisation.
+over 5 iterations with a restart after 3, 9 m^2 n + 11 m^3 with restarts every
+2, triangles halved), i.e. the matrix-core utilisation.
 ``roofline`` covers the dominant kernel, the B X product, timed live with HIP
 events at its launch boundaries inside the timed steps.
 ``elementwise`` gives the bandwidth-bound passes of the same steps (prep:
@@ -365,7 +365,8 @@ def main(argv=None):
         "ns_tflops_dense_equiv": round(dense / step_s / 1e12, 3),
         "recurrence": {"gram_space_matrices": sum(gram_space), "short_side_matrices": w.count - sum(gram_space),
                        "resident_matrices": sum(resident),
-                       "gram_restart": max(seg_len) if any(gram_space) else None},
+                       "gram_restart": {str(L): sum(1 for g, x in zip(gram_space, seg_len) if g and x == L)
+                                        for L in sorted({x for g, x in zip(gram_space, seg_len) if g})}},
         "gemm_phases": {k: {"ms": round(phase_tot[k], 4), "executed_flops": execd[k],
                             "tflops": round(execd[k] / (phase_tot[k] / 1e3) / 1e12, 1) if phase_tot[k] > 0 else None}
                         for k in execd},

@@ -110,7 +110,8 @@ typedef enum {
      * singular values far worse than the short side, and restarts bound that
      * loss.  A segment of L iterations costs 3 m^2 n + (4 L - 3) m^3 flops
      * (the short side: 3 m^2 n + m^3 per iteration), so 5 iterations as 3 + 2
-     * take 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3: cheaper whenever n > m. */
+     * take 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3: cheaper whenever n > m
+     * (as 2 + 2 + 1, 9 m^2 n + 11 m^3: cheaper once n > 1.5 m). */
     DMUON_ALGO_GRAM_SPACE = 2
 } dmuon_algo;
 
@@ -147,9 +148,11 @@ typedef struct {
                              DMUON_ALGO_GRAM_SPACE forces it on every bf16 bucket;
                              DMUON_ALGO_SHORT_SIDE forces the short side everywhere.  fp32
                              buckets always run the short side. */
-    int32_t gram_restart; /* Gram-space iterations between restarts, >= 1; 0: the default, 3.
-                             Larger values save m^2 n work and lose accuracy on
-                             ill-conditioned inputs; 1 is the short side. */
+    int32_t gram_restart; /* Gram-space iterations between restarts, >= 1; 0: the default per
+                             bucket, 2 for a padded short side up to 1024 and 3 above (the
+                             more accurate of the two on each side of that size, measured
+                             against the fp64 reference).  Larger values save m^2 n work and
+                             lose accuracy on ill-conditioned inputs; 1 is the short side. */
     const dmuon_tune_entry* tuned; /* host array of per-shape entries (NULL: none); for each bucket
                              the first entry with its key applies, entries matching no bucket are
                              ignored.  Only read during the call. */

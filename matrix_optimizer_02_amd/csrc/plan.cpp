@@ -14,7 +14,9 @@
 // by default, the Gram-space form of the recurrence (DMuon explainer on
 // gist.science, second section 2.1 Efficiente Gram Newton-Schulz Iteratie):
 // most of its products are m x m; with the default restart every 3
-// iterations, 5 iterations cost 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3.
+// iterations, 5 iterations cost 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3
+// (9 m^2 n + 11 m^3 on buckets of padded short side up to 1024, which restart
+// every 2 iterations).
 // The bucket ordering keeps the cost above.
 #include <algorithm>
 #include <climits>
@@ -52,7 +54,8 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
     if (algo_opt != DMUON_ALGO_AUTO && algo_opt != DMUON_ALGO_SHORT_SIDE && algo_opt != DMUON_ALGO_GRAM_SPACE)
         return DMUON_ERR_INVALID_ARG;
     if (opts && opts->gram_restart < 0) return DMUON_ERR_INVALID_ARG;
-    const int32_t restart = opts && opts->gram_restart > 0 ? opts->gram_restart : kDefaultGramRestart;
+    // 0: each bucket's default interval (default_gram_restart of its padded short side)
+    const int32_t restart_opt = opts ? opts->gram_restart : 0;
     const int32_t ntuned = opts ? opts->tuned_count : 0;
     if (ntuned < 0 || (ntuned > 0 && opts->tuned == nullptr)) return DMUON_ERR_INVALID_ARG;
     for (int32_t i = 0; i < count; ++i) {
@@ -115,6 +118,7 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
         // short side (their launches, not their flops, set their time).  fp32
         // buckets keep the short side.
         for (auto& bp : tmp) {
+            const int32_t restart = restart_opt > 0 ? restart_opt : default_gram_restart(bp.m_pad);
             bool gram = bp.path == kPathBF16 && algo_opt != DMUON_ALGO_SHORT_SIDE;
             if (gram && algo_opt == DMUON_ALGO_AUTO) {
                 gram = bp.n_pad > bp.m_pad && !resident_shape(bp.path, bp.m_pad, bp.n_pad);

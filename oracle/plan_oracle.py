@@ -26,8 +26,8 @@ documented contract for that step, written out plainly:
   and every member has n >= 1.5 m under the default option, on every bf16
   bucket when it is forced; the
   short-side form otherwise, and always on the f32 path.  A Gram-space bucket
-  restarts every ``gram_restart`` iterations (default 3); a short-side bucket
-  reports 1.
+  restarts every ``gram_restart`` iterations (default: 2 when its padded
+  short side is at most 1024, else 3); a short-side bucket reports 1.
 * tuned entries (per-shape configurations measured on the device, DMuon
   explainer on gist.science, sections 2.3 and 2.4): the first entry whose
   (path, padded m, padded n) matches a bucket sets its tile (which must divide
@@ -39,7 +39,13 @@ documented contract for that step, written out plainly:
 
 from __future__ import annotations
 
-DEFAULT_GRAM_RESTART = 3
+DEFAULT_GRAM_RESTART_SMALL = 2  # padded short side <= GRAM_RESTART_SMALL_MAX_M
+DEFAULT_GRAM_RESTART_LARGE = 3
+GRAM_RESTART_SMALL_MAX_M = 1024
+
+
+def default_gram_restart(m_pad: int) -> int:
+    return DEFAULT_GRAM_RESTART_SMALL if m_pad <= GRAM_RESTART_SMALL_MAX_M else DEFAULT_GRAM_RESTART_LARGE
 DEFAULT_XCD_REMAP = 4  # bit per phase: 1 Gram, 2 square, 4 B X, 8 prod
 XCD_REMAP_DEFAULT = 0xFFFFFFFF
 
@@ -111,7 +117,6 @@ def plan_reference(descs, algo: str = "auto", gram_restart: int = 0, tuned=None)
     bucket, slot, transposed, m, n, m_pad, n_pad, cost, and the list of
     buckets (path, m_pad, n_pad, members, algo, gram_restart) in execution
     order."""
-    restart = gram_restart if gram_restart > 0 else DEFAULT_GRAM_RESTART
     items = []
     keys_in_order = []
     members = {}
@@ -133,6 +138,7 @@ def plan_reference(descs, algo: str = "auto", gram_restart: int = 0, tuned=None)
     info = {}
     for key in keys_in_order:
         form = bucket_algo(key[0], key[1], key[2], [(items[i]["m"], items[i]["n"]) for i in members[key]], algo)
+        restart = gram_restart if gram_restart > 0 else default_gram_restart(key[1])
         bk = {"path": key[0], "m_pad": key[1], "n_pad": key[2], "members": list(members[key]),
               "algo": form, "gram_restart": restart if form == "gram_space" else 1,
               "tile": tile_granularity(key[0], key[1]), "xcd_remap": DEFAULT_XCD_REMAP, "cost": 0.0}

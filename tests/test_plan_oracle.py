@@ -70,14 +70,18 @@ def test_llama8b_owner_share():
 
 
 def test_recurrence_form_by_hand():
-    # (300, 700): m_pad 512 < n_pad 768, 700 >= 1.5*300 -> Gram space (restart 3)
+    # (300, 700): m_pad 512 < n_pad 768, 700 >= 1.5*300 -> Gram space, restart 2 (m_pad <= 1024)
+    # (1024, 2048): m_pad 1024, the largest short side that restarts every 2 iterations
+    # (1100, 2000): m_pad 1280 > 1024 -> Gram space, restart 3
     # (384, 500): m_pad 512, n_pad 512 -> short side
     # (200, 290): m_pad 256 < n_pad 512 but 290 < 1.5*200 = 300 -> short side (automatic rule)
     # (130, 600) f32: always short side
-    descs = [(300, 700, BF16, BF16), (384, 500, BF16, BF16), (200, 290, BF16, BF16), (130, 600, F32, F32)]
+    descs = [(300, 700, BF16, BF16), (1024, 2048, BF16, BF16), (2000, 1100, BF16, BF16), (384, 500, BF16, BF16),
+             (200, 290, BF16, BF16), (130, 600, F32, F32)]
     _, buckets = plan_reference(descs)
     form = {(b["path"], b["m_pad"], b["n_pad"]): (b["algo"], b["gram_restart"]) for b in buckets}
-    assert form == {("bf16", 512, 768): ("gram_space", 3), ("bf16", 512, 512): ("short_side", 1),
+    assert form == {("bf16", 512, 768): ("gram_space", 2), ("bf16", 1024, 2048): ("gram_space", 2),
+                    ("bf16", 1280, 2048): ("gram_space", 3), ("bf16", 512, 512): ("short_side", 1),
                     ("bf16", 256, 512): ("short_side", 1), ("f32", 192, 640): ("short_side", 1)}
     _, forced = plan_reference(descs, "gram_space", 2)
     assert {(b["path"], b["algo"], b["gram_restart"]) for b in forced} == {
