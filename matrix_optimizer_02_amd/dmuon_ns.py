@@ -309,12 +309,19 @@ def _ptr_array(ts: Sequence[torch.Tensor]):
     return arr
 
 
+def _on_current_device(t: torch.Tensor, what: str) -> None:
+    # the library addresses memory of the device current on the calling thread
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what} is on {t.device}; the current device is cuda:{torch.cuda.current_device()}")
+
+
 def _check_tensors(plan: Plan, ts: Sequence[torch.Tensor], which: str, dtype_of):
     if len(ts) != len(plan.descs):
         raise ValueError(f"{which}: expected {len(plan.descs)} tensors, got {len(ts)}")
     for i, (t, d) in enumerate(zip(ts, plan.descs)):
-        if not t.is_cuda:
-            raise ValueError(f"{which}[{i}] must be a device tensor")
+        _on_current_device(t, f"{which}[{i}]")
         if tuple(t.shape) != (d[0], d[1]) or not t.is_contiguous():
             raise ValueError(f"{which}[{i}]: expected contiguous {d[0]}x{d[1]}, got {tuple(t.shape)}")
         want = dtype_of(d)
@@ -339,6 +346,7 @@ def muon_step_batched(plan: Plan, grads: Sequence[torch.Tensor], momenta: Sequen
     _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
+    _on_current_device(workspace, "workspace")
     hp = HParams(lr, beta, weight_decay, eps, a, b, c, int(ns_steps), 1 if nesterov else 0)
     g, m, p = _ptr_array(grads), _ptr_array(momenta), _ptr_array(params)
     st = _lib.muon_step_batched(plan.handle, ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)),
@@ -358,6 +366,7 @@ def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs
     _check_tensors(plan, outputs, "outputs", lambda d: _CODE_DTYPE[d[3]])
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
+    _on_current_device(workspace, "workspace")
     i_arr, o_arr = _ptr_array(inputs), _ptr_array(outputs)
     st = _lib.ns_orthogonalize_batched(plan.handle, ctypes.cast(i_arr, ctypes.POINTER(ctypes.c_void_p)),
                                        ctypes.cast(o_arr, ctypes.POINTER(ctypes.c_void_p)),
@@ -378,7 +387,8 @@ def autotune(inputs: Sequence[torch.Tensor], out_dtypes: Optional[Sequence] = No
     out_dtypes = out_dtypes or [torch.float32] * len(inputs)
     descs = [(int(x.shape[0]), int(x.shape[1]), _code(x.dtype), _code(od)) for x, od in zip(inputs, out_dtypes)]
     for i, x in enumerate(inputs):
-        if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        _on_current_device(x, f"inputs[{i}]")
+        if not x.is_contiguous() or x.dim() != 2:
             raise ValueError(f"inputs[{i}] must be a contiguous 2-D device tensor")
     arr = _desc_array(descs)
     opts = _plan_opts(algo, gram_restart, None)
@@ -450,7 +460,8 @@ def adamw_step_batched(params: Sequence[torch.Tensor], grads: Sequence[torch.Ten
     for i in range(n):
         p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
         for name, t in (("params", p), ("grads", g), ("exp_avgs", m), ("exp_avg_sqs", v)):
-            if not t.is_cuda or not t.is_contiguous():
+            _on_current_device(t, f"{name}[{i}]")
+            if not t.is_contiguous():
                 raise ValueError(f"{name}[{i}] must be a contiguous device tensor")
         if not (p.numel() == g.numel() == m.numel() == v.numel()):
             raise ValueError(f"tensor {i}: element counts differ")
@@ -517,6 +528,7 @@ def muon_step_batched_profiled(plan: Plan, grads, momenta, params, events: Phase
     _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
+    _on_current_device(workspace, "workspace")
     hp = HParams(lr, beta, weight_decay, eps, a, b, c, events.ns_steps, 1 if nesterov else 0)
     g, m, p = _ptr_array(grads), _ptr_array(momenta), _ptr_array(params)
     vp = ctypes.POINTER(ctypes.c_void_p)
