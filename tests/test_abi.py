@@ -104,6 +104,17 @@ def test_default_algo_by_hand():
     assert p.info()[1] == 1 and p.bucket(0).algo == d.ALGO_SHORT_SIDE
 
 
+def test_default_restart_by_size():
+    # Gram-space buckets restart every 2 iterations up to a padded short side of
+    # 1024 and every 3 above; an explicit plan option or tuned entry overrides both
+    descs = [(4096, 14336, 1, 1), (1024, 4096, 1, 1), (1100, 2000, 1, 1), (2000, 1024, 1, 1), (300, 700, 1, 1)]
+    p = d.Plan(descs)
+    got = {(p.bucket(b).padded_m, p.bucket(b).padded_n): p.bucket(b).gram_restart for b in range(p.info()[1])}
+    assert got == {(4096, 14336): 3, (1024, 4096): 2, (1280, 2048): 3, (1024, 2048): 2, (512, 768): 2}
+    q = d.Plan(descs, "auto", 4)
+    assert {q.bucket(b).gram_restart for b in range(q.info()[1])} == {4}
+
+
 def test_resident_buckets_by_hand():
     # bf16, padded short side 128, padded long side <= 512, on the short side
     descs = [(128, 128, 1, 1), (100, 250, 1, 1), (512, 120, 1, 0), (128, 513, 1, 1), (129, 300, 1, 1),
