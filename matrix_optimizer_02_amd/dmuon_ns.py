@@ -201,6 +201,11 @@ class Plan:
         opts = _plan_opts(algo, gram_restart, tuning)
         _check(_lib.muon_plan_ex(arr, len(self.descs), ctypes.byref(opts), ctypes.byref(handle)), "muon_plan_ex")
         self._h = handle
+        # what every call checks its tensors against (the descriptors are valid now), computed once
+        self._sizes = [torch.Size((d[0], d[1])) for d in self.descs]
+        self._dtypes = {"grad": [_CODE_DTYPE[d[2]] for d in self.descs],
+                        "param": [_CODE_DTYPE[d[3]] for d in self.descs],
+                        "momentum": [torch.float32] * len(self.descs)}
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -317,15 +322,17 @@ def _on_current_device(t: torch.Tensor, what: str) -> None:
         raise ValueError(f"{what} is on {t.device}; the current device is cuda:{torch.cuda.current_device()}")
 
 
-def _check_tensors(plan: Plan, ts: Sequence[torch.Tensor], which: str, dtype_of):
+def _check_tensors(plan: Plan, ts: Sequence[torch.Tensor], which: str, kind: str):
+    """Every tensor on the current device, contiguous, of its descriptor's
+    shape and of the dtype `kind` ("grad", "param" or "momentum") gives it."""
     if len(ts) != len(plan.descs):
         raise ValueError(f"{which}: expected {len(plan.descs)} tensors, got {len(ts)}")
-    for i, (t, d) in enumerate(zip(ts, plan.descs)):
-        _on_current_device(t, f"{which}[{i}]")
-        if tuple(t.shape) != (d[0], d[1]) or not t.is_contiguous():
-            raise ValueError(f"{which}[{i}]: expected contiguous {d[0]}x{d[1]}, got {tuple(t.shape)}")
-        want = dtype_of(d)
-        if t.dtype != want:
+    dev = torch.cuda.current_device()
+    for i, (t, size, want) in enumerate(zip(ts, plan._sizes, plan._dtypes[kind])):
+        if t.get_device() != dev or t.dtype is not want or t.shape != size or not t.is_contiguous():
+            _on_current_device(t, f"{which}[{i}]")
+            if t.shape != size or not t.is_contiguous():
+                raise ValueError(f"{which}[{i}]: expected contiguous {size[0]}x{size[1]}, got {tuple(t.shape)}")
             raise ValueError(f"{which}[{i}]: expected {want}, got {t.dtype}")
 
 
@@ -341,9 +348,9 @@ def muon_step_batched(plan: Plan, grads: Sequence[torch.Tensor], momenta: Sequen
                       nesterov: bool = True, workspace: torch.Tensor = None, stream=None) -> None:
     """Enqueue one fused Muon step on ``stream`` (default: torch's current
     stream).  momenta and params are updated in place."""
-    _check_tensors(plan, grads, "grads", lambda d: _CODE_DTYPE[d[2]])
-    _check_tensors(plan, momenta, "momenta", lambda d: torch.float32)
-    _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
+    _check_tensors(plan, grads, "grads", "grad")
+    _check_tensors(plan, momenta, "momenta", "momentum")
+    _check_tensors(plan, params, "params", "param")
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
     _on_current_device(workspace, "workspace")
@@ -362,8 +369,8 @@ def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs
                              c: float = 2.0315, eps: float = 1e-7, workspace: torch.Tensor = None,
                              stream=None) -> None:
     """Enqueue outputs[i] = NS(inputs[i]) on ``stream``."""
-    _check_tensors(plan, inputs, "inputs", lambda d: _CODE_DTYPE[d[2]])
-    _check_tensors(plan, outputs, "outputs", lambda d: _CODE_DTYPE[d[3]])
+    _check_tensors(plan, inputs, "inputs", "grad")
+    _check_tensors(plan, outputs, "outputs", "param")
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
     _on_current_device(workspace, "workspace")
@@ -523,9 +530,9 @@ def muon_step_batched_profiled(plan: Plan, grads, momenta, params, events: Phase
                                c: float = 2.0315, nesterov: bool = True,
                                workspace: torch.Tensor = None, stream=None) -> None:
     """muon_step_batched with a HIP event recorded at every phase boundary."""
-    _check_tensors(plan, grads, "grads", lambda d: _CODE_DTYPE[d[2]])
-    _check_tensors(plan, momenta, "momenta", lambda d: torch.float32)
-    _check_tensors(plan, params, "params", lambda d: _CODE_DTYPE[d[3]])
+    _check_tensors(plan, grads, "grads", "grad")
+    _check_tensors(plan, momenta, "momenta", "momentum")
+    _check_tensors(plan, params, "params", "param")
     if workspace is None:
         raise ValueError("workspace is required (see workspace_for)")
     _on_current_device(workspace, "workspace")

@@ -427,3 +427,33 @@ int main(void) {
         r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
         assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
         assert r.stdout.split()[0] == d.version()
+
+
+def test_binding_tensor_checks(monkeypatch):
+    # the binding's per-call validation, on host tensors standing in for device
+    # ones (the current device reported as -1, the index a host tensor gives)
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: -1)
+
+    def on_current_device(t, what):
+        if t.get_device() != torch.cuda.current_device():
+            raise ValueError(f"{what} is on another device")
+
+    monkeypatch.setattr(d, "_on_current_device", on_current_device)
+    plan = d.Plan([(4, 8, 1, 0), (8, 4, 0, 1)])
+    good = {"grad": [torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(8, 4)],
+            "param": [torch.zeros(4, 8), torch.zeros(8, 4, dtype=torch.bfloat16)],
+            "momentum": [torch.zeros(4, 8), torch.zeros(8, 4)]}
+    for kind, ts in good.items():
+        d._check_tensors(plan, ts, kind, kind)
+    with pytest.raises(ValueError, match="expected 2 tensors"):
+        d._check_tensors(plan, good["grad"][:1], "grads", "grad")
+    with pytest.raises(ValueError, match=r"grads\[1\]: expected torch.float32"):
+        d._check_tensors(plan, [good["grad"][0], torch.zeros(8, 4, dtype=torch.bfloat16)], "grads", "grad")
+    with pytest.raises(ValueError, match=r"params\[0\]: expected contiguous 4x8"):
+        d._check_tensors(plan, [torch.zeros(8, 4).t(), good["param"][1]], "params", "param")
+    with pytest.raises(ValueError, match=r"momenta\[1\]: expected contiguous 8x4"):
+        d._check_tensors(plan, [good["momentum"][0], torch.zeros(4, 8)], "momenta", "momentum")
+    # a tensor on another device than the current one
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    with pytest.raises(ValueError, match=r"grads\[0\] is on another device"):
+        d._check_tensors(plan, good["grad"], "grads", "grad")
