@@ -178,6 +178,36 @@ def test_resident_buckets(ns_steps):
         assert rel(f64(outs[i]), ref) < TOL["bf16"], (RESIDENT_SHAPES[i], rel(f64(outs[i]), ref))
 
 
+# More buckets than one grouped launch's segment table holds (24): 30 bf16 shapes
+# that pad to 30 distinct (m, n) buckets, wide and tall alternating, so every
+# phase of the 256-tile class goes out as two launches; both forms of the
+# recurrence run (near-square buckets stay on the short side), and 26 fp32
+# shapes do the same for the fp32 class.
+MANY_BF16 = [((m, n) if k % 2 == 0 else (n, m))
+             for k, (m, n) in enumerate((m, n_pad - 37) for m, base in ((140, 256), (300, 512), (520, 768))
+                                        for n_pad in range(base, base + 2560, 256))]
+MANY_F32 = [(m, m + 64 * j + 5) for m in (40, 100) for j in range(13)]
+
+
+@pytest.mark.parametrize("path", ["bf16", "f32"])
+def test_more_buckets_than_one_launch_holds(path):
+    shapes = MANY_BF16 if path == "bf16" else MANY_F32
+    w = custom_workload(f"many_{path}", shapes, path, "f32")
+    say(f"case {len(shapes)} buckets ({path}) muon_step_batched fp32 zero params")
+    host, out, G, *_ = step_gpu(w, seed=21, zero_params=True)
+    plan = d.plan_for(G, [torch.float32] * len(G))
+    assert plan.info()[1] == len(shapes) > 24
+    if path == "bf16":
+        algos = {plan.bucket(b).algo for b in range(plan.info()[1])}
+        assert algos == {d.ALGO_GRAM_SPACE, d.ALGO_SHORT_SIDE}
+    for i, (r, c) in enumerate(shapes):
+        ref = oracle.muon_step(host["G"][i], host["M"][i], host["W"][i], lr=LR, beta=BETA, eps=EPS)
+        s_upd = oracle.update_scale(r, c)
+        assert rel(out["M"][i], ref["M_new"]) < 1e-6, (r, c)
+        e = rel(-out["W"][i] / (LR * s_upd), ref["O"])
+        assert e < TOL[path], ((r, c), e)
+
+
 @pytest.mark.parametrize("name", sorted(SHAPE_SETS))
 def test_step_shapes(name):
     shapes, dt = SHAPE_SETS[name]
