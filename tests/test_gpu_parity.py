@@ -496,3 +496,60 @@ def test_full_size_orthogonalize_sampled(wname, algo):
         assert e < TOL["bf16"]
     del G, outs
     torch.cuda.empty_cache()
+
+
+# ---- beyond 2^31 elements in one matrix ---------------------------------------------
+#
+# A matrix that is zero except for a few dense blocks in distinct rows and
+# columns is, up to a permutation of rows and columns, block diagonal; the
+# Newton-Schulz iteration keeps that structure (every product of block-diagonal
+# matrices is block diagonal, p(0) = 0) and commutes with the permutation, and
+# the Frobenius normalisation sees only the blocks.  So the full-size output is
+# the oracle's output on the small block-diagonal matrix of the same blocks,
+# scattered back, and exactly zero everywhere else.  Two matrices of 16500 x
+# 131200 (2.16e9 elements, a wide and a tall one) put blocks past element 2^31.
+BIG_BLOCKS = [(0, 0, 64, 200), (8000, 70000, 100, 150), (16400, 130900, 50, 300)]  # row, col, rows, cols
+
+
+def test_beyond_2_31_elements_block_structure():
+    r, c = 16500, 131200
+    rng = np.random.default_rng(31)
+    blocks = [torch.from_numpy(rng.standard_normal((br, bc)).astype(np.float32)).to(torch.bfloat16)
+              for (_, _, br, bc) in BIG_BLOCKS]
+    # the small block-diagonal matrix the oracle sees
+    sr, sc = sum(b[2] for b in BIG_BLOCKS), sum(b[3] for b in BIG_BLOCKS)
+    small = np.zeros((sr, sc))
+    pos = []
+    i0 = j0 = 0
+    for blk, (_, _, br, bc) in zip(blocks, BIG_BLOCKS):
+        small[i0:i0 + br, j0:j0 + bc] = f64(blk)
+        pos.append((i0, j0))
+        i0, j0 = i0 + br, j0 + bc
+    ref = oracle.newton_schulz(small, 5, A, B, C, EPS)
+    say(f"case {r}x{c} and {c}x{r} bf16 ({r * c} elements each) muon_step_batched, fp32 zero params")
+    G = [torch.zeros(r, c, dtype=torch.bfloat16, device="cuda"), torch.zeros(c, r, dtype=torch.bfloat16, device="cuda")]
+    for blk, (br0, bc0, br, bc) in zip(blocks, BIG_BLOCKS):
+        G[0][br0:br0 + br, bc0:bc0 + bc] = blk.cuda()
+        G[1][bc0:bc0 + bc, br0:br0 + br] = blk.t().cuda()  # the tall matrix holds the transposed blocks
+    M = [torch.zeros(x.shape, device="cuda") for x in G]
+    W = [torch.zeros(x.shape, device="cuda") for x in G]
+    plan = d.plan_for(G, [torch.float32] * 2)
+    ws = d.workspace_for(plan)
+    d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, workspace=ws)
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert torch.equal(M[k], G[k].float())  # M' = 0.95 * 0 + G, exactly
+        s_upd = oracle.update_scale(*W[k].shape)
+        got = np.zeros((sr, sc))
+        for (br0, bc0, br, bc), (i0, j0) in zip(BIG_BLOCKS, pos):
+            if k == 0:
+                got[i0:i0 + br, j0:j0 + bc] = f64(W[0][br0:br0 + br, bc0:bc0 + bc]) / (-LR * s_upd)
+            else:
+                got[i0:i0 + br, j0:j0 + bc] = f64(W[1][bc0:bc0 + bc, br0:br0 + br]).T / (-LR * s_upd)
+        # every nonzero of W' lies in a block
+        assert int(torch.count_nonzero(W[k])) == int(np.count_nonzero(got))
+        e = rel(got, ref)
+        say(f"  {'wide' if k == 0 else 'tall'}: rel err {e:.3e}")
+        assert e < TOL["bf16"]
+    del G, M, W, ws
+    torch.cuda.empty_cache()
