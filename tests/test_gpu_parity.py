@@ -139,7 +139,7 @@ SHAPE_SETS = {
     "bf16_ragged": ([(300, 700), (700, 300), (129, 257), (1000, 130), (64, 64), (1, 513), (513, 1),
                      (128, 128), (200, 72)], "bf16"),
     "bf16_multi_tile": ([(1024, 1536), (1536, 1024), (768, 768), (520, 1300)], "bf16"),
-    "f32_ragged": ([(70, 33), (33, 70), (200, 200), (1, 65), (130, 250)], "f32"),
+    "f32_ragged": ([(70, 33), (33, 70), (200, 200), (1, 65), (130, 250), (1, 1)], "f32"),
 }
 
 
@@ -159,9 +159,9 @@ def test_orthogonalize_shapes(name, ns_steps, algo):
 
 
 # every padded long side the resident kernel takes (128 .. 512), wide, tall, square,
-# ragged and single-row
+# ragged, single-row and 1 x 1
 RESIDENT_SHAPES = [(128, 128), (100, 250), (77, 300), (120, 512), (512, 128), (300, 77), (1, 200), (64, 64),
-                   (128, 384), (37, 129)]
+                   (128, 384), (37, 129), (1, 1)]
 
 
 @pytest.mark.parametrize("ns_steps", [1, 2, 5])
