@@ -4,7 +4,7 @@
 // mirrored stores, and X' = s (a X + B X) into the other X copy (computed as
 // X'^T tiles: rows of the long side, columns of the short side).  Products are
 // computed with fp32 FMA on 64 x 64 tiles, 256 threads, 4 x 4 outputs per
-// thread, K staged through LDS 16 at a time.
+// thread, K staged through two LDS stages 16 at a time.
 //
 // Page basis: as for the bf16 kernels -- X X^T on the full matrix, one
 // triangle of the symmetric products (DMuon explainer on gist.science, second
@@ -30,8 +30,11 @@ __device__ __forceinline__ void tri_decode_f(int t, int tm, int& I, int& J) {
 
 template <int PHASE>
 __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
-    __shared__ float Ps[kBKf][kT + 4];
-    __shared__ float Qs[kBKf][kT + 4];
+    // two LDS stages: slab k + 1 is fetched into registers while slab k is
+    // multiplied, then written to the other stage, so one barrier per slab
+    // suffices and the global load latency overlaps the FMAs
+    __shared__ float Ps[2][kBKf][kT + 4];
+    __shared__ float Qs[2][kBKf][kT + 4];
 
     const int bid = blockIdx.x;
     int s = 0;
@@ -63,24 +66,36 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
 
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int lrow = tid >> 2, lk = (tid & 3) * 4;
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < K; k0 += kBKf) {
+    const int kk = tid >> 4, jj = (tid & 15) * 4;  // B X: X row k0 + kk, long-side columns jj .. jj + 3
+    auto fetch = [&](int64_t k0, float4& pv, float4& qv) {
+        if (PHASE == kBX)
+            pv = *reinterpret_cast<const float4*>(P + (k0 + kk) * sg.n_pad + (int64_t)I * kT + jj);
+        else
+            pv = *reinterpret_cast<const float4*>(P + ((int64_t)I * kT + lrow) * ldk + k0 + lk);
+        qv = *reinterpret_cast<const float4*>(Qt + lrow * ldk + k0 + lk);
+    };
+    auto stage = [&](int b, const float4& pv, const float4& qv) {
         if (PHASE == kBX) {
-            // P[j][k] = X[k][j]: X rows k0 .. k0+15, long-side columns of tile I
-            const int kk = tid >> 4, jj = (tid & 15) * 4;
-            const float4 pv = *reinterpret_cast<const float4*>(P + (k0 + kk) * sg.n_pad + (int64_t)I * kT + jj);
-            Ps[kk][jj + 0] = pv.x; Ps[kk][jj + 1] = pv.y; Ps[kk][jj + 2] = pv.z; Ps[kk][jj + 3] = pv.w;
+            // P[j][k] = X[k][j]
+            Ps[b][kk][jj + 0] = pv.x; Ps[b][kk][jj + 1] = pv.y; Ps[b][kk][jj + 2] = pv.z; Ps[b][kk][jj + 3] = pv.w;
         } else {
-            const float4 pv = *reinterpret_cast<const float4*>(P + ((int64_t)I * kT + lrow) * ldk + k0 + lk);
-            Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
+            Ps[b][lk + 0][lrow] = pv.x; Ps[b][lk + 1][lrow] = pv.y; Ps[b][lk + 2][lrow] = pv.z; Ps[b][lk + 3][lrow] = pv.w;
         }
-        const float4 qv = *reinterpret_cast<const float4*>(Qt + lrow * ldk + k0 + lk);
-        Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
-        __syncthreads();
+        Qs[b][lk + 0][lrow] = qv.x; Qs[b][lk + 1][lrow] = qv.y; Qs[b][lk + 2][lrow] = qv.z; Qs[b][lk + 3][lrow] = qv.w;
+    };
+    float acc[4][4] = {};
+    float4 pv, qv;
+    fetch(0, pv, qv);
+    stage(0, pv, qv);
+    __syncthreads();
+    int b = 0;
+    for (int64_t k0 = 0; k0 < K; k0 += kBKf) {
+        const bool more = k0 + kBKf < K;
+        if (more) fetch(k0 + kBKf, pv, qv);
         #pragma unroll
         for (int k = 0; k < kBKf; ++k) {
-            const float4 av = *reinterpret_cast<const float4*>(&Ps[k][ty * 4]);
-            const float4 bv = *reinterpret_cast<const float4*>(&Qs[k][tx * 4]);
+            const float4 av = *reinterpret_cast<const float4*>(&Ps[b][k][ty * 4]);
+            const float4 bv = *reinterpret_cast<const float4*>(&Qs[b][k][tx * 4]);
             const float ar[4] = {av.x, av.y, av.z, av.w};
             const float br[4] = {bv.x, bv.y, bv.z, bv.w};
             #pragma unroll
@@ -88,7 +103,11 @@ __global__ __launch_bounds__(256) void ns_gemm_f32_kernel(GemmArgs args) {
                 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
         }
+        // stage b ^ 1 was last read in the previous slab, before the barrier
+        // that ended it; every thread is done with stage b after this one
+        if (more) stage(b ^ 1, pv, qv);
         __syncthreads();
+        b ^= 1;
     }
 
     // thread owns rows ty*4 + i and columns tx*4 + j of the 64 x 64 tile
