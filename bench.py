@@ -322,26 +322,42 @@ def main(argv=None):
     gram_space = [plan.bucket(plan.query(i).bucket).algo == d.ALGO_GRAM_SPACE for i in range(w.count)]
     resident = [plan.bucket(plan.query(i).bucket).resident for i in range(w.count)]
     alg = dense = 0
-    execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}
+    execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}  # grouped launches
+    res_flops = 0  # the resident kernel's (every iteration of a small bucket in one launch)
     for s, L, res in zip(w.matrices, seg_len, resident):
         m, n = min(s.rows, s.cols), max(s.rows, s.cols)
         alg += NS_STEPS * algorithmic_flops(m, n)
         dense += NS_STEPS * dense_flops(m, n)
         for k, v in executed_flops(m, n, L, resident=res).items():
-            execd[k] += v
-    executed = sum(execd.values())
+            if res:
+                res_flops += v
+            else:
+                execd[k] += v
+    executed = sum(execd.values()) + res_flops
     step_s = ms_per_step / 1e3
     value = alg / step_s / 1e12
-    peak = BF16_PEAK_TFLOPS if paths == {"bf16"} else FP32_PEAK_TFLOPS
-    # B X phases that launch anything: iteration k closes a segment of some bucket
-    bx_iters = [k for k in range(NS_STEPS) if any(k % L == L - 1 or k == NS_STEPS - 1 for L in set(seg_len))]
-    bx_ms = [p[names.index(f"bx{k}")] for p in per for k in bx_iters]
-    bx_avg = sum(bx_ms) / len(bx_ms)
-    bxf = execd["bx"] / len(bx_iters)  # per B X phase (one grouped launch per tile class)
-    achieved = bxf / (bx_avg / 1e3) / 1e12
+    f32_only = paths == {"f32"}
+    peak = FP32_PEAK_TFLOPS if f32_only else BF16_PEAK_TFLOPS
     phase_tot = {k: sum(p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) == k) / len(per)
                  for k in execd}
-    traffic = read_traffic("bx_gemm_bf16_llama8b") if args.workload == "llama3.1-8b_owner_1of8" else None
+    grouped_len = {L for L, res in zip(seg_len, resident) if not res}
+    if grouped_len:
+        # the dominant kernel, B X: the phases that launch anything (iteration k
+        # closes a segment of some bucket that runs in the grouped launches)
+        bx_iters = [k for k in range(NS_STEPS) if any(k % L == L - 1 or k == NS_STEPS - 1 for L in grouped_len)]
+        bx_ms = [p[names.index(f"bx{k}")] for p in per for k in bx_iters]
+        launch_ms = sum(bx_ms) / len(bx_ms)
+        flops_per_launch = execd["bx"] / len(bx_iters)  # per B X phase (one grouped launch per tile class)
+        kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X))" if f32_only
+                  else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)")
+    else:
+        # every bucket resident: one launch per step, timed within iteration 0's Gram phase
+        launch_ms = avg["gram0"]
+        flops_per_launch = res_flops
+        kernel = "ns_resident_kernel (every iteration of a small bf16 bucket in one launch, the matrix in LDS)"
+    achieved = flops_per_launch / (launch_ms / 1e3) / 1e12
+    traffic = (read_traffic("bx_gemm_bf16_llama8b")
+               if args.workload == "llama3.1-8b_owner_1of8" and not args.tuning_cache else None)
 
     out = {
         "metric": "NS TFLOP/s and % bf16 MFMA peak, Muon step ms for Llama-3-8B owner share",
@@ -370,13 +386,16 @@ def main(argv=None):
         "gemm_phases": {k: {"ms": round(phase_tot[k], 4), "executed_flops": execd[k],
                             "tflops": round(execd[k] / (phase_tot[k] / 1e3) / 1e12, 1) if phase_tot[k] > 0 else None}
                         for k in execd},
+        "resident": ({"matrices": sum(resident), "executed_flops": res_flops,
+                      "timed_in": "gram0 (its launch follows prep, before iteration 0's grouped Gram)"}
+                     if res_flops else None),
         "matrices_per_s": round(w.count / step_s, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
         "gemm_ms_per_step": round(sum(gemm_ms) / len(per), 4),
-        "roofline": {"bound": "mfma", "kernel": "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)",
+        "roofline": {"bound": "alu" if f32_only else "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "launch_ms": round(bx_avg, 4), "flops_per_launch": bxf},
+                     "launch_ms": round(launch_ms, 4), "flops_per_launch": flops_per_launch},
     }
     # the bandwidth-bound passes of the same steps, against the HBM roofline
     elems = w.elements()
