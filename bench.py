@@ -86,6 +86,26 @@ def executed_flops(m: int, n: int, seg_len: int, steps: int = NS_STEPS, resident
     return out
 
 
+def dominant_kernel(seg_len, resident, bx_flops_grouped, res_flops, bx_ms_per_step, gram0_ms, f32_only,
+                    steps: int = NS_STEPS):
+    """(kernel name, average launch ms, flops per launch) of the kernel the
+    roofline covers.  With any bucket in the grouped launches it is the B X
+    product: the B X phases that launch anything are the iterations that close
+    a segment of such a bucket (every iteration on the short side), each one
+    grouped launch per tile class.  With every bucket resident it is the
+    resident kernel, one launch per step, timed inside iteration 0's Gram
+    phase.  bx_ms_per_step holds each timed step's B X phase times."""
+    grouped_len = {L for L, res in zip(seg_len, resident) if not res}
+    if grouped_len:
+        bx_iters = [k for k in range(steps) if any(k % L == L - 1 or k == steps - 1 for L in grouped_len)]
+        bx_ms = [row[k] for row in bx_ms_per_step for k in bx_iters]
+        kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X))" if f32_only
+                  else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)")
+        return kernel, sum(bx_ms) / len(bx_ms), bx_flops_grouped / len(bx_iters)
+    return ("ns_resident_kernel (every iteration of a small bf16 bucket in one launch, the matrix in LDS)",
+            gram0_ms, res_flops)
+
+
 def read_traffic(kernel_tag: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source (sha256 recorded in the summary)."""
@@ -340,21 +360,9 @@ def main(argv=None):
     peak = FP32_PEAK_TFLOPS if f32_only else BF16_PEAK_TFLOPS
     phase_tot = {k: sum(p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) == k) / len(per)
                  for k in execd}
-    grouped_len = {L for L, res in zip(seg_len, resident) if not res}
-    if grouped_len:
-        # the dominant kernel, B X: the phases that launch anything (iteration k
-        # closes a segment of some bucket that runs in the grouped launches)
-        bx_iters = [k for k in range(NS_STEPS) if any(k % L == L - 1 or k == NS_STEPS - 1 for L in grouped_len)]
-        bx_ms = [p[names.index(f"bx{k}")] for p in per for k in bx_iters]
-        launch_ms = sum(bx_ms) / len(bx_ms)
-        flops_per_launch = execd["bx"] / len(bx_iters)  # per B X phase (one grouped launch per tile class)
-        kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X))" if f32_only
-                  else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)")
-    else:
-        # every bucket resident: one launch per step, timed within iteration 0's Gram phase
-        launch_ms = avg["gram0"]
-        flops_per_launch = res_flops
-        kernel = "ns_resident_kernel (every iteration of a small bf16 bucket in one launch, the matrix in LDS)"
+    kernel, launch_ms, flops_per_launch = dominant_kernel(
+        seg_len, resident, execd["bx"], res_flops, [[p[names.index(f"bx{k}")] for k in range(NS_STEPS)] for p in per],
+        avg["gram0"], f32_only)
     achieved = flops_per_launch / (launch_ms / 1e3) / 1e12
     traffic = (read_traffic("bx_gemm_bf16_llama8b")
                if args.workload == "llama3.1-8b_owner_1of8" and not args.tuning_cache else None)

@@ -82,3 +82,23 @@ def test_resident_counts_whole_products():
     m, n = 100, 400
     ex = bench.executed_flops(m, n, 1, resident=True)
     assert ex == {"gram": 5 * 2 * m * m * n, "square": 5 * 2 * m ** 3, "prod": 0, "bx": 5 * 2 * m * m * n}
+
+
+def test_dominant_kernel_choice():
+    # grouped buckets restarting every 3 and every 2 iterations plus a short-side one:
+    # B X launches in iterations 0 .. 4 (short side every iteration)
+    rows = [[1.0, 2.0, 3.0, 4.0, 5.0], [1.0, 2.0, 3.0, 4.0, 5.0]]
+    k, ms, fl = bench.dominant_kernel([3, 2, 1], [False, False, False], 50.0, 0, rows, 9.0, False)
+    assert "bf16" in k and ms == 3.0 and fl == 10.0
+    # Gram space only, every 3 iterations: segments close in iterations 2 and 4
+    k, ms, fl = bench.dominant_kernel([3, 3], [False, False], 40.0, 0, rows, 9.0, False)
+    assert ms == 4.0 and fl == 20.0
+    # fp32 only: the SIMT kernel
+    k, ms, fl = bench.dominant_kernel([1], [False], 50.0, 0, rows, 9.0, True)
+    assert "f32" in k and ms == 3.0
+    # every bucket resident: the resident launch, timed inside iteration 0's Gram phase
+    k, ms, fl = bench.dominant_kernel([1, 1], [True, True], 0.0, 7.0, rows, 9.0, False)
+    assert "resident" in k and ms == 9.0 and fl == 7.0
+    # resident buckets beside grouped ones leave the B X accounting to the grouped ones
+    k, ms, fl = bench.dominant_kernel([1, 3], [True, False], 30.0, 7.0, rows, 9.0, False)
+    assert "bf16" in k and ms == 4.0 and fl == 15.0
