@@ -32,9 +32,14 @@
  *    they only enqueue work on `stream` (a hipStream_t, NULL = the default
  *    stream) and return.  Buffers must stay alive until the stream has passed
  *    that point.
- *  - Arguments are checked before anything is enqueued: on an error return
- *    nothing has been enqueued.  A launch failure returns DMUON_ERR_HIP (work
- *    enqueued before it may have run).
+ *  - Arguments are checked before anything is enqueued, and every host
+ *    allocation of a call is made before its first enqueue: on an
+ *    INVALID_ARG, UNSUPPORTED, WORKSPACE or ALLOC return nothing has been
+ *    enqueued.  A launch failure returns DMUON_ERR_HIP (work enqueued before
+ *    it may have run).
+ *  - No buffer a call writes (momentum, parameter, output, workspace) may
+ *    overlap any other buffer of the call, byte range against byte range;
+ *    read-only inputs may overlap each other.  Violations are INVALID_ARG.
  *  - Results are deterministic: same plan, inputs and device give bitwise
  *    identical outputs (no floating-point atomics).
  *  - NaN and Inf in the inputs are not masked; they propagate.
@@ -63,7 +68,7 @@ typedef enum {
     DMUON_ERR_UNSUPPORTED = -2, /* valid request outside the library's limits (e.g. a dim >= 2^30) */
     DMUON_ERR_WORKSPACE = -3,   /* workspace missing, too small or not 256-byte aligned */
     DMUON_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-    DMUON_ERR_ALLOC = -5        /* host allocation failed (plan creation) */
+    DMUON_ERR_ALLOC = -5        /* host allocation failed (nothing was enqueued) */
 } dmuon_status;
 
 typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype;
@@ -129,7 +134,11 @@ typedef struct {
     int64_t padded_m;        /* key: padded short side */
     int64_t padded_n;        /* key: padded long side */
     int32_t algo;            /* dmuon_algo for the bucket; DMUON_ALGO_AUTO: the plan option's rule.
-                                DMUON_ALGO_GRAM_SPACE is accepted on the bf16 path only */
+                                DMUON_ALGO_GRAM_SPACE is accepted on the bf16 path only; under
+                                the DMUON_ALGO_AUTO plan option it applies only to a bucket that
+                                the automatic rule would run in the Gram space (entries are keyed
+                                by padded dims, so the bucket's real members may differ from
+                                those it was measured on), else the bucket keeps the short side */
     int32_t gram_restart;    /* Gram-space iterations between restarts; 0: the plan option's */
     uint32_t xcd_remap;      /* bf16 path: bit per phase (1 Gram, 2 square, 4 B X, 8 prod) whose launch
                                 gives each XCD a contiguous run of the bucket's tiles (neighbouring tiles
@@ -142,9 +151,10 @@ typedef struct {
 
 typedef struct {
     int32_t algo;         /* dmuon_algo; DMUON_ALGO_AUTO (the default) picks the Gram space for
-                             bf16 buckets with padded n > padded m whose members all have
-                             n >= 1.5 m, except resident ones (padded m 128, padded n <= 512:
-                             see muon_plan_bucket_resident), else the short side;
+                             bf16 buckets with padded n > padded m and padded m >= 1024 whose
+                             members all have n >= 3 m (in bf16 the Gram space resolves small
+                             singular values worse; there it saves the most work for the
+                             least accuracy), else the short side;
                              DMUON_ALGO_GRAM_SPACE forces it on every bf16 bucket;
                              DMUON_ALGO_SHORT_SIDE forces the short side everywhere.  fp32
                              buckets always run the short side. */
@@ -159,7 +169,12 @@ typedef struct {
     int32_t tuned_count;
 } dmuon_plan_opts;
 
-/* Build the batch plan (host only, no device work).  Per matrix: m = min(rows,
+/* Build the batch plan (host only, no device work): step one of the owner's
+ * work, which batches matrices of similar shape so that their Newton-Schulz
+ * iterations run jointly and amortise kernel dispatch (DMuon explainer on
+ * gist.science, second section 2.1, "Batching"), and orders the work by its
+ * computational cost, as owners are balanced by cost (DMuon abstract; the
+ * explainer's section 2.3 on load balancing).  Per matrix: m = min(rows,
  * cols), n = max(rows, cols), transposed = rows > cols (square matrices are
  * not transposed).  Tile granularity g = 64 on the fp32 path; on the bf16 path
  * g = 128 when m <= 128, else 256.  Padded dims are m, n rounded up to g (the
@@ -197,7 +212,10 @@ DMUON_API dmuon_status muon_plan_info(const dmuon_plan* plan, int32_t* count, in
 
 /* Per-matrix plan entry: bucket index (execution order), slot within the
  * bucket, transposed flag, padded short/long dims, and the dense NS cost
- * 4 m^2 n + 2 m^3 of the real shape.  Any output pointer may be NULL.
+ * 4 m^2 n + 2 m^3 of the real shape, the cost by which the work is balanced
+ * (DMuon abstract; DMuon explainer on gist.science, section 2.3).  The cost
+ * is an exact integer (int64), and the slot is reported as well, for tests
+ * that check the plan element by element.  Any output pointer may be NULL.
  * INVALID_ARG for idx outside [0, count). */
 DMUON_API dmuon_status muon_plan_query(const dmuon_plan* plan, int32_t idx, int32_t* bucket, int32_t* slot,
                              int32_t* transposed, int64_t* padded_m, int64_t* padded_n,
@@ -261,10 +279,15 @@ DMUON_API dmuon_status muon_autotune(const dmuon_matrix_desc* descs, int32_t cou
 /* Release a plan (NULL is a no-op). */
 DMUON_API void muon_plan_destroy(dmuon_plan* plan);
 
-/* One fused Muon step over every matrix of the plan: momentum (in place in
- * momenta[i], fp32), normalisation, ns_steps NS iterations on the short side,
- * and the in-place parameter update of params[i] (param_dtype; bf16 results
- * are rounded to nearest even once, from fp32).
+/* One fused Muon step over every matrix of the plan: the owner's whole work
+ * on each of its matrices -- the Newton-Schulz iteration and the optimizer
+ * update, once, on the full matrix (DMuon abstract; DMuon explainer on
+ * gist.science, section 2.1 Owner-Centric Executiestrategie) -- applied to
+ * the momentum-aggregated gradient (explainer, section 1).  Momentum (in
+ * place in momenta[i], fp32), normalisation, ns_steps NS iterations on the
+ * short side (or in the Gram space, per bucket: dmuon_algo), and the
+ * in-place parameter update of params[i] (param_dtype; bf16 results are
+ * rounded to nearest even once, from fp32).
  *   grads[i]   device, rows x cols, grad_dtype, read only, must not alias
  *   momenta[i] device, rows x cols, fp32, read and written
  *   params[i]  device, rows x cols, param_dtype, read and written
@@ -272,13 +295,17 @@ DMUON_API void muon_plan_destroy(dmuon_plan* plan);
  *   workspace  device, >= muon_plan_workspace_bytes, 256-byte aligned
  *   stream     hipStream_t (NULL = default stream)
  * Errors: INVALID_ARG (null plan/hp/array/pointer, misaligned pointer,
- * ns_steps < 0), WORKSPACE, HIP. */
+ * ns_steps < 0, overlapping buffers), WORKSPACE, ALLOC, HIP. */
 DMUON_API dmuon_status muon_step_batched(const dmuon_plan* plan, const void* const* grads,
                                float* const* momenta, void* const* params,
                                const dmuon_hparams* hp, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Orthogonalise every matrix of the plan without momentum or update:
+/* Orthogonalise every matrix of the plan without momentum or update: the
+ * Newton-Schulz iteration alone, which drives the singular values of each
+ * input towards a uniform spectrum (DMuon explainer on gist.science, section
+ * 1), on the short side or in the m x m Gram space with X X^T computed as one
+ * triangle (explainer, second section 2.1).
  * outputs[i] = NS(inputs[i]) with ns_steps iterations of coefficients
  * (a, b, c) after normalisation by ||input||_F + eps, in the input's own
  * orientation.  inputs[i] are device rows x cols in grad_dtype (read only);

@@ -23,6 +23,50 @@ namespace {
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A caller buffer's byte range and whether the call writes it.
+struct Span {
+    uintptr_t lo, hi;
+    bool written;
+};
+
+// True when no two of the spans overlap where one of them is written.  Read-
+// only spans may overlap each other (the same gradient passed twice is
+// harmless).  Sorted by start, a span overlaps an earlier one exactly when it
+// starts below that one's end, so one sweep suffices.
+bool disjoint_where_written(std::vector<Span>& v) {
+    std::sort(v.begin(), v.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
+    uintptr_t end_any = 0, end_written = 0;
+    for (const Span& sp : v) {
+        if (sp.lo < end_written || (sp.written && sp.lo < end_any)) return false;
+        end_any = std::max(end_any, sp.hi);
+        if (sp.written) end_written = std::max(end_written, sp.hi);
+    }
+    return true;
+}
+
+size_t dtype_bytes(int32_t dt) { return dt == DMUON_BF16 ? 2 : 4; }
+
+// The matrices' byte ranges for an overlap check: read-only sources, fp32
+// momenta (when given) and destinations, and the workspace the plan uses.
+bool args_disjoint(const dmuon_plan* plan, const void* const* src, float* const* mom, const void* const* dst,
+                   const void* workspace) {
+    std::vector<Span> v;
+    v.reserve(3 * plan->mats.size() + 1);
+    for (size_t i = 0; i < plan->mats.size(); ++i) {
+        const MatPlan& mp = plan->mats[i];
+        const uintptr_t e = (uintptr_t)(mp.rows * mp.cols);
+        auto add = [&](const void* p, size_t esz, bool w) {
+            v.push_back({reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + e * esz, w});
+        };
+        add(src[i], dtype_bytes(mp.grad_dtype), false);
+        if (mom) add(mom[i], 4, true);
+        add(dst[i], dtype_bytes(mp.param_dtype), true);
+    }
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
+    v.push_back({w0, w0 + plan->workspace_bytes, true});
+    return disjoint_where_written(v);
+}
+
 struct StepParams {
     const void* const* src;
     float* const* mom;     // nullptr: orthogonalisation
@@ -32,19 +76,28 @@ struct StepParams {
     int ns_steps, nesterov;
 };
 
-dmuon_status check_common(const dmuon_plan* plan, const void* const* src, const void* const* dst,
-                          void* workspace, size_t workspace_bytes) {
+// Checks shared by the step and orthogonalisation entry points (mom ==
+// nullptr: orthogonalisation).  Every pointer non-null and 16-byte aligned,
+// the workspace large enough and 256-byte aligned, and no written buffer
+// (momentum, destination, workspace) overlapping any other buffer of the call.
+dmuon_status check_call(const dmuon_plan* plan, const void* const* src, float* const* mom, bool need_mom,
+                        const void* const* dst, void* workspace, size_t workspace_bytes) {
     if (plan == nullptr) return DMUON_ERR_INVALID_ARG;
     const size_t count = plan->mats.size();
     if (count == 0) return DMUON_OK;
-    if (src == nullptr || dst == nullptr) return DMUON_ERR_INVALID_ARG;
+    if (src == nullptr || dst == nullptr || (need_mom && mom == nullptr)) return DMUON_ERR_INVALID_ARG;
     for (size_t i = 0; i < count; ++i) {
-        if (!aligned16(src[i]) || !aligned16(dst[i])) return DMUON_ERR_INVALID_ARG;
-        if (src[i] == dst[i]) return DMUON_ERR_INVALID_ARG;
+        if (!aligned16(src[i]) || !aligned16(dst[i]) || (need_mom && !aligned16(mom[i])))
+            return DMUON_ERR_INVALID_ARG;
     }
     if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0 ||
         workspace_bytes < plan->workspace_bytes)
         return DMUON_ERR_WORKSPACE;
+    try {
+        if (!args_disjoint(plan, src, need_mom ? mom : nullptr, dst, workspace)) return DMUON_ERR_INVALID_ARG;
+    } catch (...) {
+        return DMUON_ERR_ALLOC;
+    }
     return DMUON_OK;
 }
 
@@ -133,13 +186,15 @@ int32_t seg_len_for(const BucketPlan& bp, const StepParams& sp) {
 dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
                       void* const* events);
 
-// The enqueue sequence behind every step entry point; host allocation
-// failures come back as a status, never as an exception across the ABI.
+// The enqueue sequence behind every step entry point.  run_impl makes every
+// host allocation of the call before its first enqueue, so a failed one
+// (the only exceptions it can raise) comes back as ALLOC with nothing
+// enqueued, and no exception crosses the ABI.
 dmuon_status run(const dmuon_plan* p, const StepParams& sp, void* workspace, hipStream_t stream,
                  void* const* events = nullptr) {
     try {
         return run_impl(p, sp, workspace, stream, events);
-    } catch (const std::bad_alloc&) {
+    } catch (...) {
         return DMUON_ERR_ALLOC;
     }
 }
@@ -157,7 +212,6 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         if (events == nullptr) return true;
         return hipEventRecord(static_cast<hipEvent_t>(events[ev++]), stream) == hipSuccess;
     };
-    if (!mark()) return DMUON_ERR_HIP;
     char* ws = static_cast<char*>(workspace);
     DevMatRec* table = reinterpret_cast<DevMatRec*>(ws + p->off_records);
     float* scale = reinterpret_cast<float*>(ws + p->off_scale);
@@ -177,6 +231,15 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         }
     }
 
+    // Every host container of the call, sized now: nothing below allocates
+    // once the first launch is enqueued.
+    std::vector<Roles> roles(nb);
+    std::vector<int32_t> xcur(nb, 0);  // X copy holding the current iterate
+    std::vector<int32_t> j(nb), lc(nb);
+    std::vector<SegSpec> segs;
+    segs.reserve(2 * nb);  // a phase takes at most two products per bucket
+
+    if (!mark()) return DMUON_ERR_HIP;
     // per-matrix records, plan order, written into the workspace by small launches
     RecChunk chunk{};
     chunk.table = table;
@@ -244,8 +307,6 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     //   j < Lc - 1: T = A Q_j, then A = Q_j T
     //   j = Lc - 1: X' = s P_Lc X into the other X copy
     // so a segment of one iteration is exactly the short-side iteration.
-    std::vector<Roles> roles(nb);
-    std::vector<int32_t> xcur(nb, 0);  // X copy holding the current iterate
     for (size_t b = 0; b < nb; ++b) {
         const BucketPlan& bp = p->buckets[b];
         roles[b] = Roles{(int64_t)bp.off_a, (int64_t)bp.off_b, (int64_t)bp.off_g[0], (int64_t)bp.off_g[1],
@@ -254,15 +315,12 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     auto xoff = [&](size_t b, int copy) {
         return (int64_t)(copy == 0 ? p->buckets[b].off_x0 : p->buckets[b].off_x1);
     };
-    std::vector<SegSpec> segs;
-    segs.reserve(2 * nb);
     auto phase_done = [&](int phase) -> bool {
         const bool ok = launch_segs(ws, scale, sp, phase, segs, stream) == hipSuccess;
         segs.clear();
         return ok;
     };
     for (int it = 0; it < steps; ++it) {
-        std::vector<int32_t> j(nb), lc(nb);
         for (size_t b = 0; b < nb; ++b) {
             j[b] = it % seg[b];
             lc[b] = std::min(seg[b], steps - (it - j[b]));
@@ -329,13 +387,8 @@ extern "C" dmuon_status muon_step_batched(const dmuon_plan* plan, const void* co
                                           const dmuon_hparams* hp, void* workspace,
                                           size_t workspace_bytes, void* stream) {
     if (plan == nullptr || hp == nullptr || hp->ns_steps < 0) return DMUON_ERR_INVALID_ARG;
-    dmuon_status st = check_common(plan, grads, params, workspace, workspace_bytes);
+    dmuon_status st = check_call(plan, grads, momenta, true, params, workspace, workspace_bytes);
     if (st != DMUON_OK || plan->mats.empty()) return st;
-    if (momenta == nullptr) return DMUON_ERR_INVALID_ARG;
-    for (size_t i = 0; i < plan->mats.size(); ++i) {
-        if (!aligned16(momenta[i])) return DMUON_ERR_INVALID_ARG;
-        if (momenta[i] == grads[i] || momenta[i] == params[i]) return DMUON_ERR_INVALID_ARG;
-    }
     StepParams sp{grads, momenta, params, 1, hp->lr, hp->beta, hp->weight_decay, hp->eps,
                   hp->a, hp->b, hp->c, hp->ns_steps, hp->nesterov};
     return run(plan, sp, workspace, static_cast<hipStream_t>(stream));
@@ -346,7 +399,7 @@ extern "C" dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const v
                                                  float b, float c, float eps, void* workspace,
                                                  size_t workspace_bytes, void* stream) {
     if (plan == nullptr || ns_steps < 0) return DMUON_ERR_INVALID_ARG;
-    dmuon_status st = check_common(plan, inputs, outputs, workspace, workspace_bytes);
+    dmuon_status st = check_call(plan, inputs, nullptr, false, outputs, workspace, workspace_bytes);
     if (st != DMUON_OK || plan->mats.empty()) return st;
     StepParams sp{inputs, nullptr, outputs, 0, 0.f, 0.f, 0.f, eps, a, b, c, ns_steps, 0};
     return run(plan, sp, workspace, static_cast<hipStream_t>(stream));
@@ -366,13 +419,8 @@ extern "C" dmuon_status muon_step_batched_profiled(const dmuon_plan* plan, const
         return DMUON_ERR_INVALID_ARG;
     for (int32_t i = 0; i < num_events; ++i)
         if (events[i] == nullptr) return DMUON_ERR_INVALID_ARG;
-    dmuon_status st = check_common(plan, grads, params, workspace, workspace_bytes);
+    dmuon_status st = check_call(plan, grads, momenta, true, params, workspace, workspace_bytes);
     if (st != DMUON_OK || plan->mats.empty()) return st;
-    if (momenta == nullptr) return DMUON_ERR_INVALID_ARG;
-    for (size_t i = 0; i < plan->mats.size(); ++i) {
-        if (!aligned16(momenta[i])) return DMUON_ERR_INVALID_ARG;
-        if (momenta[i] == grads[i] || momenta[i] == params[i]) return DMUON_ERR_INVALID_ARG;
-    }
     StepParams sp{grads, momenta, params, 1, hp->lr, hp->beta, hp->weight_decay, hp->eps,
                   hp->a, hp->b, hp->c, hp->ns_steps, hp->nesterov};
     return run(plan, sp, workspace, static_cast<hipStream_t>(stream), events);
@@ -429,10 +477,40 @@ extern "C" dmuon_status adamw_step_batched(int32_t count, const int64_t* numels,
         if (numels[i] == 0) continue;
         if (!aligned16(params[i]) || !aligned16(grads[i]) || !aligned16(exp_avgs[i]) || !aligned16(exp_avg_sqs[i]))
             return DMUON_ERR_INVALID_ARG;
-        const void* q[4] = {params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]};
-        for (int x = 0; x < 4; ++x)
-            for (int y = x + 1; y < 4; ++y)
-                if (q[x] == q[y]) return DMUON_ERR_INVALID_ARG;
+    }
+    // no written buffer (parameter, moments) may overlap another buffer of the call
+    try {
+        std::vector<Span> v;
+        v.reserve(4 * (size_t)count);
+        for (int32_t i = 0; i < count; ++i) {
+            if (numels[i] == 0) continue;
+            const uintptr_t n = (uintptr_t)numels[i];
+            auto add = [&](const void* q, size_t esz, bool w) {
+                v.push_back({reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + n * esz, w});
+            };
+            add(params[i], dtype_bytes(param_dtypes[i]), true);
+            add(grads[i], dtype_bytes(grad_dtypes[i]), false);
+            add(exp_avgs[i], 4, true);
+            add(exp_avg_sqs[i], 4, true);
+        }
+        if (!disjoint_where_written(v)) return DMUON_ERR_INVALID_ARG;
+    } catch (...) {
+        return DMUON_ERR_ALLOC;
+    }
+    // every launch's block count fits the grid, checked before the first one
+    // is enqueued (the launches below group the tensors the same way)
+    {
+        int32_t i = 0;
+        while (i < count) {
+            int32_t n = 0;
+            int64_t blocks = 0;
+            for (; i < count && n < kAdamChunk; ++i) {
+                if (numels[i] == 0) continue;
+                ++n;
+                blocks += (numels[i] + kAdamBlock - 1) / kAdamBlock;
+            }
+            if (blocks > (int64_t)0x7fffffff) return DMUON_ERR_UNSUPPORTED;
+        }
     }
     // bias corrections in double on the host, handed to the kernel in fp32
     const double t = (double)hp->step;
@@ -464,7 +542,6 @@ extern "C" dmuon_status adamw_step_batched(int32_t count, const int64_t* numels,
             r.g_dtype = grad_dtypes[i];
             a.total_blocks += (numels[i] + kAdamBlock - 1) / kAdamBlock;
         }
-        if (a.total_blocks > (int64_t)0x7fffffff) return DMUON_ERR_UNSUPPORTED;
         if (launch_adamw(a, s) != hipSuccess) return DMUON_ERR_HIP;
     }
     return DMUON_OK;

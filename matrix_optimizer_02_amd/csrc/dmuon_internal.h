@@ -29,6 +29,21 @@ constexpr int64_t kGramRestartSmallMaxM = 1024;
 inline int32_t default_gram_restart(int64_t m_pad) {
     return m_pad <= kGramRestartSmallMaxM ? kDefaultGramRestartSmall : kDefaultGramRestartLarge;
 }
+// The automatic rule's accuracy guard for the Gram-space form.  In bf16 the
+// Gram space resolves small singular values worse than the short side, and
+// it saves the least work where it loses the most accuracy: near-square
+// matrices (at n = 1.5 m it executes 11-14% fewer flops for about 1.5 times
+// the short side's error) and small short sides (whose products are latency-
+// rather than flop-bound).  Measured against the fp64 oracle on Gaussian
+// inputs, every bucket of padded short side >= 1024 whose members have
+// n >= 3 m stays within 1.2e-2 relative error; the default therefore takes
+// the Gram space only there.
+constexpr int64_t kGramMinPaddedM = 1024;
+constexpr int64_t kGramMinAspect = 3;
+inline bool gram_auto_shape(int path, int64_t m_pad, int64_t n_pad) {
+    return path == kPathBF16 && n_pad > m_pad && m_pad >= kGramMinPaddedM;
+}
+inline bool gram_auto_member(int64_t m, int64_t n) { return n >= kGramMinAspect * m; }
 // Phases whose launch deals each XCD a contiguous run of a bucket's tiles by
 // default: the B X product (bit 2), whose X panels are then reused in that
 // XCD's L2.

@@ -10,13 +10,13 @@
 // cost of one iteration on an m x n matrix (m <= n) is taken as
 // 4 m^2 n + 2 m^3: the products X X^T, A A and B X.
 //
-// Each bf16 bucket whose padded long side exceeds its padded short side runs,
-// by default, the Gram-space form of the recurrence (DMuon explainer on
-// gist.science, second section 2.1 Efficiente Gram Newton-Schulz Iteratie):
-// most of its products are m x m; with the default restart every 3
-// iterations, 5 iterations cost 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3
-// (9 m^2 n + 11 m^3 on buckets of padded short side up to 1024, which restart
-// every 2 iterations).
+// Each bf16 bucket of padded short side >= 1024 whose matrices all have a long
+// side of at least three times the short one runs, by default, the Gram-space
+// form of the recurrence (DMuon explainer on gist.science, second section 2.1
+// Efficiente Gram Newton-Schulz Iteratie): most of its products are m x m;
+// with the default restart every 3 iterations, 5 iterations cost
+// 6 m^2 n + 14 m^3 instead of 15 m^2 n + 5 m^3 (9 m^2 n + 11 m^3 on buckets of
+// padded short side 1024, which restart every 2 iterations).
 // The bucket ordering keeps the cost above.
 #include <algorithm>
 #include <climits>
@@ -110,20 +110,22 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
             tmp[b].members.push_back(i);
         }
         // Recurrence form.  The Gram space does less work once the padded long
-        // side exceeds the padded short one; by default it is also kept off
-        // buckets holding a matrix whose real long side is under 1.5 times its
-        // short side (a near-square matrix has small singular values, which the
-        // Gram space resolves worse, and there it saves little), and off the
-        // buckets small enough to run all their iterations in one launch on the
-        // short side (their launches, not their flops, set their time).  fp32
-        // buckets keep the short side.
+        // side exceeds the padded short one.  By default it is kept to buckets
+        // of padded short side >= 1024 whose every member has n >= 3 m (the
+        // accuracy guard of gram_auto_shape / gram_auto_member): a near-square
+        // matrix has small singular values, which the Gram space resolves
+        // worse, and there it saves little; a small short side's products are
+        // latency-bound, so the flops it saves buy little time.  fp32 buckets
+        // keep the short side.
+        auto auto_gram = [&](const BucketPlan& bp) {
+            bool ok = gram_auto_shape(bp.path, bp.m_pad, bp.n_pad);
+            for (int32_t i : bp.members) ok = ok && gram_auto_member(p->mats[i].m, p->mats[i].n);
+            return ok;
+        };
         for (auto& bp : tmp) {
             const int32_t restart = restart_opt > 0 ? restart_opt : default_gram_restart(bp.m_pad);
             bool gram = bp.path == kPathBF16 && algo_opt != DMUON_ALGO_SHORT_SIDE;
-            if (gram && algo_opt == DMUON_ALGO_AUTO) {
-                gram = bp.n_pad > bp.m_pad && !resident_shape(bp.path, bp.m_pad, bp.n_pad);
-                for (int32_t i : bp.members) gram = gram && 2 * p->mats[i].n >= 3 * p->mats[i].m;
-            }
+            if (gram && algo_opt == DMUON_ALGO_AUTO) gram = auto_gram(bp);
             bp.algo = gram ? DMUON_ALGO_GRAM_SPACE : DMUON_ALGO_SHORT_SIDE;
             bp.seg_len = gram ? restart : 1;
             bp.xcd_mask = kDefaultXcdMask;
@@ -144,7 +146,13 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
                 e->reserved != 0 || !(e->cost_ms_per_matrix >= 0.0))
                 throw InvalidEntry();
             if (e->tile != 0) bp.tile = e->tile;
-            if (e->algo != DMUON_ALGO_AUTO) {
+            // Entries are keyed by padded dims, so one measured on some shapes
+            // may meet a bucket whose real members fail the automatic rule's
+            // accuracy guard (2047 x 3000 pads like 2000 x 3000): under the
+            // automatic option such a bucket keeps the short side.
+            const bool entry_gram_refused =
+                e->algo == DMUON_ALGO_GRAM_SPACE && algo_opt == DMUON_ALGO_AUTO && !auto_gram(bp);
+            if (e->algo != DMUON_ALGO_AUTO && !entry_gram_refused) {
                 bp.algo = e->algo;
                 bp.seg_len = e->algo == DMUON_ALGO_GRAM_SPACE ? restart : 1;
             }

@@ -22,18 +22,20 @@ documented contract for that step, written out plainly:
 * the reported per-matrix cost is 4 m^2 n + 2 m^3 of the real shape;
 * recurrence form per bucket: the Gram-space form (the iteration carried in
   the m x m Gram space, DMuon explainer on gist.science, second section 2.1
-  Efficiente Gram Newton-Schulz Iteratie) on the bf16 path when n_pad > m_pad
-  and every member has n >= 1.5 m under the default option, on every bf16
-  bucket when it is forced; the
-  short-side form otherwise, and always on the f32 path.  A Gram-space bucket
-  restarts every ``gram_restart`` iterations (default: 2 when its padded
-  short side is at most 1024, else 3); a short-side bucket reports 1.
+  Efficiente Gram Newton-Schulz Iteratie) on the bf16 path when n_pad > m_pad,
+  m_pad >= 1024 and every member has n >= 3 m under the default option, on
+  every bf16 bucket when it is forced; the short-side form otherwise, and
+  always on the f32 path.  A Gram-space bucket restarts every
+  ``gram_restart`` iterations (default: 2 when its padded short side is at
+  most 1024, else 3); a short-side bucket reports 1.
 * tuned entries (per-shape configurations measured on the device, DMuon
   explainer on gist.science, sections 2.3 and 2.4): the first entry whose
   (path, padded m, padded n) matches a bucket sets its tile (which must divide
   both padded dims; 128 or 256 on bf16, 64 on f32), its form (not the Gram
-  space on f32) and restart, and its XCD remap bits (default: B X only, bit
-  4).  When every bucket carries a measured per-matrix cost > 0, buckets are
+  space on f32; under the default option an entry's Gram space is refused,
+  and the automatic form kept, for a bucket that the default rule keeps on
+  the short side) and restart, and its XCD remap bits (default: B X only,
+  bit 4).  When every bucket carries a measured per-matrix cost > 0, buckets are
   ordered by count times that cost instead of the dense cost.
 """
 
@@ -42,6 +44,8 @@ from __future__ import annotations
 DEFAULT_GRAM_RESTART_SMALL = 2  # padded short side <= GRAM_RESTART_SMALL_MAX_M
 DEFAULT_GRAM_RESTART_LARGE = 3
 GRAM_RESTART_SMALL_MAX_M = 1024
+GRAM_MIN_PADDED_M = 1024  # the default rule's Gram space: padded short side at least this
+GRAM_MIN_ASPECT = 3       # ... and every member's long side at least this many short sides
 
 
 def default_gram_restart(m_pad: int) -> int:
@@ -74,16 +78,15 @@ def bucket_algo(path: str, m_pad: int, n_pad: int, shapes, option: str = "auto")
         return "short_side"
     if option == "gram_space":
         return "gram_space"
-    if m_pad == 128 and n_pad <= 512:  # small enough to run every iteration in one launch
-        return "short_side"
-    if n_pad > m_pad and all(n >= 1.5 * m for m, n in shapes):
+    if n_pad > m_pad and m_pad >= GRAM_MIN_PADDED_M and all(n >= GRAM_MIN_ASPECT * m for m, n in shapes):
         return "gram_space"
     return "short_side"
 
 
-def _apply_entry(bucket, e, option_restart):
+def _apply_entry(bucket, e, option_restart, option="auto", shapes=()):
     """Apply tuned entry e (dict with the library's field names and codes:
-    path 0/1, algo 0 auto / 1 short side / 2 Gram space) to bucket."""
+    path 0/1, algo 0 auto / 1 short side / 2 Gram space) to bucket, whose
+    members have the real (m, n) in ``shapes``."""
     tile = e.get("tile", 0)
     allowed = (128, 256) if bucket["path"] == "bf16" else (64,)
     if tile and (tile not in allowed or bucket["m_pad"] % tile or bucket["n_pad"] % tile):
@@ -101,6 +104,9 @@ def _apply_entry(bucket, e, option_restart):
         raise ValueError("remap bits")
     if tile:
         bucket["tile"] = tile
+    if (form == "gram_space" and option == "auto"
+            and bucket_algo(bucket["path"], bucket["m_pad"], bucket["n_pad"], shapes, "auto") != "gram_space"):
+        form = None  # the default rule's accuracy guard keeps this bucket on the short side
     if form is not None:
         bucket["algo"] = form
         bucket["gram_restart"] = option_restart if form == "gram_space" else 1
@@ -145,7 +151,7 @@ def plan_reference(descs, algo: str = "auto", gram_restart: int = 0, tuned=None)
         code = DTYPE_BF16 if key[0] == "bf16" else DTYPE_F32
         for e in tuned or []:
             if (e["path"], e["padded_m"], e["padded_n"]) == (code, key[1], key[2]):
-                _apply_entry(bk, e, restart)
+                _apply_entry(bk, e, restart, algo, [(items[i]["m"], items[i]["n"]) for i in members[key]])
                 break
         info[key] = bk
     measured = bool(keys_in_order) and all(info[k]["cost"] > 0 for k in keys_in_order)

@@ -87,31 +87,42 @@ def test_plan_matches_reference(name, algo, restart):
 
 
 def test_default_algo_by_hand():
-    # bf16: Gram space exactly when the padded long side exceeds the padded short side
-    # whose members all have n >= 1.5 m, except for buckets of padded short side 128
-    # and padded long side <= 512 (every iteration in one launch, on the short side)
-    p = d.Plan([(4096, 14336, 1, 1), (4096, 4096, 1, 1), (1024, 4096, 0, 0), (200, 256, 1, 1),
-                (128, 192, 1, 1), (100, 250, 1, 1), (384, 1000, 1, 1), (300, 1000, 1, 1),
-                (100, 700, 1, 1), (512, 120, 1, 1)])
+    # bf16: Gram space exactly when the padded long side exceeds the padded short side,
+    # the padded short side is at least 1024 and every member has n >= 3 m
+    p = d.Plan([(4096, 14336, 1, 1), (4096, 4096, 1, 1), (1024, 4096, 0, 0), (1024, 4096, 1, 1),
+                (200, 256, 1, 1), (128, 192, 1, 1), (100, 250, 1, 1), (384, 1000, 1, 1), (100, 700, 1, 1),
+                (512, 120, 1, 1), (1100, 3000, 1, 1), (3400, 1100, 1, 1), (768, 3072, 1, 1)])
     got = {(p.bucket(b).padded_m, p.bucket(b).padded_n, p.bucket(b).path): p.bucket(b).algo
            for b in range(p.info()[1])}
     assert got == {(4096, 14336, 1): d.ALGO_GRAM_SPACE, (4096, 4096, 1): d.ALGO_SHORT_SIDE,
-                   (1024, 4096, 0): d.ALGO_SHORT_SIDE, (256, 256, 1): d.ALGO_SHORT_SIDE,
-                   (128, 256, 1): d.ALGO_SHORT_SIDE, (512, 1024, 1): d.ALGO_GRAM_SPACE,
-                   (128, 768, 1): d.ALGO_GRAM_SPACE, (128, 512, 1): d.ALGO_SHORT_SIDE}
-    # one near-square member keeps its whole bucket on the short side
-    p = d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)])
+                   (1024, 4096, 0): d.ALGO_SHORT_SIDE, (1024, 4096, 1): d.ALGO_GRAM_SPACE,
+                   (256, 256, 1): d.ALGO_SHORT_SIDE, (128, 256, 1): d.ALGO_SHORT_SIDE,
+                   (512, 1024, 1): d.ALGO_SHORT_SIDE, (128, 768, 1): d.ALGO_SHORT_SIDE,
+                   (128, 512, 1): d.ALGO_SHORT_SIDE, (1280, 3072, 1): d.ALGO_SHORT_SIDE,
+                   (1280, 3584, 1): d.ALGO_GRAM_SPACE, (768, 3072, 1): d.ALGO_SHORT_SIDE}
+    # one member with n < 3 m keeps its whole bucket on the short side
+    p = d.Plan([(1100, 3400, 1, 1), (1150, 3400, 1, 1)])
     assert p.info()[1] == 1 and p.bucket(0).algo == d.ALGO_SHORT_SIDE
+
+
+def test_tuned_gram_entry_respects_the_default_rule():
+    # an entry's Gram space applies under the default option only where the default
+    # rule would take it on the bucket's real members (entries are keyed by padded dims)
+    e = d.TuneEntry(path=1, tile=0, padded_m=1280, padded_n=3584, algo=d.ALGO_GRAM_SPACE, gram_restart=2,
+                    xcd_remap=d.XCD_REMAP_DEFAULT)
+    assert d.Plan([(1100, 3400, 1, 1)], tuning=[e]).bucket(0).algo == d.ALGO_GRAM_SPACE
+    assert d.Plan([(1150, 3400, 1, 1)], tuning=[e]).bucket(0).algo == d.ALGO_SHORT_SIDE
+    assert d.Plan([(1150, 3400, 1, 1)], "gram_space", tuning=[e]).bucket(0).algo == d.ALGO_GRAM_SPACE
 
 
 def test_default_restart_by_size():
     # Gram-space buckets restart every 2 iterations up to a padded short side of
     # 1024 and every 3 above; an explicit plan option or tuned entry overrides both
-    descs = [(4096, 14336, 1, 1), (1024, 4096, 1, 1), (1100, 2000, 1, 1), (2000, 1024, 1, 1), (300, 700, 1, 1)]
+    descs = [(4096, 14336, 1, 1), (1024, 4096, 1, 1), (1100, 4000, 1, 1), (3072, 1024, 1, 1), (300, 700, 1, 1)]
     p = d.Plan(descs)
     got = {(p.bucket(b).padded_m, p.bucket(b).padded_n): p.bucket(b).gram_restart for b in range(p.info()[1])}
-    assert got == {(4096, 14336): 3, (1024, 4096): 2, (1280, 2048): 3, (1024, 2048): 2, (512, 768): 2}
-    q = d.Plan(descs, "auto", 4)
+    assert got == {(4096, 14336): 3, (1024, 4096): 2, (1280, 4096): 3, (1024, 3072): 2, (512, 768): 1}
+    q = d.Plan(descs, "gram_space", 4)
     assert {q.bucket(b).gram_restart for b in range(q.info()[1])} == {4}
 
 
@@ -212,11 +223,11 @@ def test_tuning_cache_round_trip(tmp_path):
 
 def test_autotune_argument_errors():
     need = ctypes.c_size_t()
-    arr = (d.MatrixDesc * 1)(d.MatrixDesc(256, 512, 1, 1))
+    arr = (d.MatrixDesc * 1)(d.MatrixDesc(1024, 4096, 1, 1))
     assert LIB.muon_autotune_workspace_bytes(arr, 1, None, None) == d.DMUON_ERR_INVALID_ARG
     assert LIB.muon_autotune_workspace_bytes(arr, 1, None, ctypes.byref(need)) == d.DMUON_OK
     # the trial plans include the Gram-space one, whose workspace is the largest
-    assert need.value >= d.Plan([(256, 512, 1, 1)], "gram_space").workspace_bytes()
+    assert need.value >= d.Plan([(1024, 4096, 1, 1)], "gram_space").workspace_bytes()
     # several buckets: the final whole-batch trials run every bucket at once
     multi = [(128, 128, 1, 1)] * 3 + [(128, 512, 1, 1)] * 4 + [(768, 256, 1, 1)] * 2 + [(96, 160, 0, 0)]
     marr = (d.MatrixDesc * len(multi))(*[d.MatrixDesc(*x) for x in multi])
@@ -246,7 +257,7 @@ def test_workspace_covers_operands():
             need += cnt * es * 3 * bk["m_pad"] ** 2
     assert d.Plan(descs).workspace_bytes() >= need
     # forcing the short side needs no Gram-space arrays, forcing the Gram space more
-    assert d.Plan(descs, "short_side").workspace_bytes() < d.Plan(descs).workspace_bytes()
+    assert d.Plan(descs, "short_side").workspace_bytes() < d.Plan(descs, "gram_space").workspace_bytes()
     assert d.Plan(descs, "gram_space").workspace_bytes() > d.Plan(descs).workspace_bytes()
     assert d.Plan([]).workspace_bytes() == 0
 
@@ -325,7 +336,20 @@ def test_step_argument_errors_before_device_work():
                 None) == d.DMUON_ERR_WORKSPACE
     hp_bad = d.HParams(0.02, 0.95, 0.0, 1e-7, 3.4445, -4.775, 2.0315, -1, 1)
     assert step(p.handle, g, m, w, ctypes.byref(hp_bad), ws, ws_bytes, None) == d.DMUON_ERR_INVALID_ARG
+    # Byte ranges, not just pointers: the 8 x 16 matrices are 256 B in bf16 (grads,
+    # params) and 512 B in fp32 (momenta).  No written buffer may overlap another.
+    inside = lambda base, off: base + off
+    assert step(p.handle, g, m, _arr([0x50000, inside(0x50000, 128)]), ctypes.byref(hp), ws, ws_bytes,
+                None) == d.DMUON_ERR_INVALID_ARG  # params[1] starts inside params[0]
+    assert step(p.handle, _arr([inside(0x30000, 256), 0x20000]), m, w, ctypes.byref(hp), ws, ws_bytes,
+                None) == d.DMUON_ERR_INVALID_ARG  # grads[0] inside momenta[0]
+    assert step(p.handle, g, _arr([0x30000, inside(0x1000000, 64)]), w, ctypes.byref(hp), ws, ws_bytes,
+                None) == d.DMUON_ERR_INVALID_ARG  # momenta[1] inside the workspace
+    assert step(p.handle, _arr([0x1000000 - 128, 0x20000]), m, w, ctypes.byref(hp), ws, ws_bytes,
+                None) == d.DMUON_ERR_INVALID_ARG  # grads[0] runs into the workspace
     ortho = LIB.ns_orthogonalize_batched
+    assert ortho(p.handle, g, _arr([0x50000, inside(0x10000, 16)]), 5, 3.4445, -4.775, 2.0315, 1e-7, ws, ws_bytes,
+                 None) == d.DMUON_ERR_INVALID_ARG  # outputs[1] inside inputs[0]
     assert ortho(p.handle, g, w, -1, 3.4445, -4.775, 2.0315, 1e-7, ws, ws_bytes, None) == d.DMUON_ERR_INVALID_ARG
     assert ortho(p.handle, g, g, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, ws_bytes, None) == d.DMUON_ERR_INVALID_ARG
     assert ortho(p.handle, g, w, 5, 3.4445, -4.775, 2.0315, 1e-7, ws, 16, None) == d.DMUON_ERR_WORKSPACE
@@ -354,6 +378,9 @@ def test_adamw_argument_errors_before_device_work():
     assert f(2, n, pd, gd, _arr([0x10004, 0x20000]), G, M, V, ctypes.byref(hp), None) == E  # misaligned
     assert f(2, n, pd, gd, P, _arr([0x10000, 0x40000]), M, V, ctypes.byref(hp), None) == E  # g aliases p
     assert f(2, n, pd, gd, P, G, M, _arr([0x50000, 0x80000]), ctypes.byref(hp), None) == E  # v aliases m
+    # byte ranges: tensor 0 holds 100 elements (200 B of bf16 params, 400 B of fp32 moments)
+    assert f(2, n, pd, gd, P, G, _arr([0x50000, 0x50000 + 256]), V, ctypes.byref(hp), None) == E  # m[1] in m[0]
+    assert f(2, n, pd, gd, P, _arr([0x10000 + 64, 0x40000]), M, V, ctypes.byref(hp), None) == E  # g[0] in p[0]
     # count 0 and all-empty tensors enqueue nothing
     assert f(0, None, None, None, None, None, None, None, ctypes.byref(hp), None) == d.DMUON_OK
     z = (ctypes.c_int64 * 2)(0, 0)

@@ -70,22 +70,29 @@ def test_llama8b_owner_share():
 
 
 def test_recurrence_form_by_hand():
-    # (300, 700): m_pad 512 < n_pad 768, 700 >= 1.5*300 -> Gram space, restart 2 (m_pad <= 1024)
-    # (1024, 2048): m_pad 1024, the largest short side that restarts every 2 iterations
-    # (1100, 2000): m_pad 1280 > 1024 -> Gram space, restart 3
-    # (384, 500): m_pad 512, n_pad 512 -> short side
-    # (200, 290): m_pad 256 < n_pad 512 but 290 < 1.5*200 = 300 -> short side (automatic rule)
-    # (130, 600) f32: always short side
-    descs = [(300, 700, BF16, BF16), (1024, 2048, BF16, BF16), (2000, 1100, BF16, BF16), (384, 500, BF16, BF16),
-             (200, 290, BF16, BF16), (130, 600, F32, F32)]
+    # Default rule: Gram space for bf16 buckets with n_pad > m_pad, m_pad >= 1024 and every member n >= 3 m.
+    # (300, 700): m_pad 512 < 1024 -> short side
+    # (1024, 4096): m_pad 1024, 4096 >= 3*1024 -> Gram space, restart 2 (m_pad <= 1024)
+    # (3400, 1100): m 1100 -> m_pad 1280, n 3400 -> n_pad 3584, 3400 >= 3300 -> Gram space, restart 3
+    # (1100, 3200): m_pad 1280, n_pad 3328, 3200 < 3300 -> short side
+    # (768, 3072): m_pad 768 < 1024 -> short side
+    # (384, 500): m_pad 512 = n_pad 512 -> short side
+    # (130, 600) f32: always short side (g = 64: 192 x 640)
+    descs = [(300, 700, BF16, BF16), (1024, 4096, BF16, BF16), (3400, 1100, BF16, BF16), (1100, 3200, BF16, BF16),
+             (768, 3072, BF16, BF16), (384, 500, BF16, BF16), (130, 600, F32, F32)]
     _, buckets = plan_reference(descs)
     form = {(b["path"], b["m_pad"], b["n_pad"]): (b["algo"], b["gram_restart"]) for b in buckets}
-    assert form == {("bf16", 512, 768): ("gram_space", 2), ("bf16", 1024, 2048): ("gram_space", 2),
-                    ("bf16", 1280, 2048): ("gram_space", 3), ("bf16", 512, 512): ("short_side", 1),
-                    ("bf16", 256, 512): ("short_side", 1), ("f32", 192, 640): ("short_side", 1)}
+    assert form == {("bf16", 512, 768): ("short_side", 1), ("bf16", 1024, 4096): ("gram_space", 2),
+                    ("bf16", 1280, 3584): ("gram_space", 3), ("bf16", 1280, 3328): ("short_side", 1),
+                    ("bf16", 768, 3072): ("short_side", 1), ("bf16", 512, 512): ("short_side", 1),
+                    ("f32", 192, 640): ("short_side", 1)}
     _, forced = plan_reference(descs, "gram_space", 2)
     assert {(b["path"], b["algo"], b["gram_restart"]) for b in forced} == {
         ("bf16", "gram_space", 2), ("f32", "short_side", 1)}
+    # one member with n < 3 m keeps its whole bucket on the short side:
+    # (1100, 3400) and (1150, 3400) both pad to 1280 x 3584; 3400 < 3 * 1150
+    _, mixed = plan_reference([(1100, 3400, BF16, BF16), (1150, 3400, BF16, BF16)])
+    assert [(b["m_pad"], b["n_pad"], b["algo"]) for b in mixed] == [(1280, 3584, "short_side")]
 
 
 def test_tuned_entries_by_hand():
@@ -105,3 +112,16 @@ def test_tuned_entries_by_hand():
     # one bucket without a cost: the dense order stays
     _, b2 = plan_reference(descs, tuned=tuned[:2])
     assert [b["m_pad"] for b in b2] == [1024, 256, 128]
+    # Entries are keyed by padded dims: under the default option an entry's Gram space
+    # applies only where the default rule would take it on the bucket's real members.
+    # (1100, 3400) and (1150, 3400) pad alike (1280 x 3584); only the first has n >= 3 m.
+    g = [e(1280, 3584, algo=2, gram_restart=2)]
+    _, ok = plan_reference([(1100, 3400, BF16, BF16)], tuned=g)
+    _, refused = plan_reference([(1150, 3400, BF16, BF16)], tuned=g)
+    _, forced = plan_reference([(1150, 3400, BF16, BF16)], "gram_space", tuned=g)
+    assert [(b["algo"], b["gram_restart"]) for b in ok] == [("gram_space", 2)]
+    assert [(b["algo"], b["gram_restart"]) for b in refused] == [("short_side", 1)]
+    assert [(b["algo"], b["gram_restart"]) for b in forced] == [("gram_space", 2)]
+    # the same for an entry on a bucket whose padded short side is under 1024
+    _, small = plan_reference([(256, 1536, BF16, BF16)], tuned=[e(256, 1536, algo=2)])
+    assert [b["algo"] for b in small] == ["short_side"]
