@@ -316,6 +316,24 @@ DMUON_API dmuon_status ns_orthogonalize_batched(const dmuon_plan* plan, const vo
                                       float c, float eps, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ---- the step for callers that cannot allocate ------------------------------
+ * For callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The step of muon_step_batched, with its workspace taken from a
+ * static device array of DMUON_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * The caller passes the inputs and outputs as for muon_step_batched.  Every
+ * call on a GPU shares that GPU's array, so calls on one GPU that overlap in
+ * time (other streams, other threads) race and must be serialised by the
+ * caller.  Errors as for muon_step_batched; WORKSPACE when the plan needs more
+ * than DMUON_NOALLOC_SCRATCH_BYTES (muon_plan_workspace_bytes), UNSUPPORTED
+ * for a device index beyond 255, HIP if the array's address cannot be found. */
+#define DMUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+DMUON_API dmuon_status muon_step_batched_noalloc(const dmuon_plan* plan, const void* const* grads,
+                                                 float* const* momenta, void* const* params,
+                                                 const dmuon_hparams* hp, void* stream);
+
 /* ---- AdamW for the parameters that do not go through Muon -------------------
  * The optimizer takes a separate AdamW learning rate for the parameters that
  * its predicate does not route to Muon (DMuon project documentation,

@@ -10,6 +10,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -545,4 +546,58 @@ extern "C" dmuon_status adamw_step_batched(int32_t count, const int64_t* numels,
         if (launch_adamw(a, s) != hipSuccess) return DMUON_ERR_HIP;
     }
     return DMUON_OK;
+}
+
+// ---- the step without any allocation ---------------------------------------------
+// For callers that cannot allocate device memory: the workspace is this
+// file-scope device array, one copy per GPU, held from the library's load on
+// that GPU until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address hipGetSymbolAddress gives for the current GPU, looked up once
+// per GPU on the entry point's first call there.  Every call on a GPU shares
+// that GPU's array: calls on one GPU that overlap in time race on it.  No part
+// of it needs to start at zero (every kernel writes what it later reads).
+static __device__ __align__(256) char scratch[DMUON_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device, null until looked up
+
+dmuon_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DMUON_ERR_HIP;
+    if (dev >= kMaxScratchDevices) return DMUON_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return DMUON_ERR_HIP;
+        if ((reinterpret_cast<uintptr_t>(ptr) & (kAlign - 1)) != 0) return DMUON_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DMUON_OK;
+}
+
+}  // namespace
+
+extern "C" dmuon_status muon_step_batched_noalloc(const dmuon_plan* plan, const void* const* grads,
+                                                  float* const* momenta, void* const* params,
+                                                  const dmuon_hparams* hp, void* stream) {
+    if (plan == nullptr || hp == nullptr || hp->ns_steps < 0) return DMUON_ERR_INVALID_ARG;
+    if (plan->mats.empty()) return DMUON_OK;
+    if (plan->workspace_bytes > (size_t)DMUON_NOALLOC_SCRATCH_BYTES) return DMUON_ERR_WORKSPACE;
+    void* ws = nullptr;
+    try {
+        const dmuon_status st = scratch_of_current_device(&ws);
+        if (st != DMUON_OK) return st;
+    } catch (...) {  // the lock
+        return DMUON_ERR_HIP;
+    }
+    dmuon_status st = check_call(plan, grads, momenta, true, params, ws, DMUON_NOALLOC_SCRATCH_BYTES);
+    if (st != DMUON_OK) return st;
+    StepParams sp{grads, momenta, params, 1, hp->lr, hp->beta, hp->weight_decay, hp->eps,
+                  hp->a, hp->b, hp->c, hp->ns_steps, hp->nesterov};
+    return run(plan, sp, ws, static_cast<hipStream_t>(stream));
 }

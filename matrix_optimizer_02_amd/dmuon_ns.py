@@ -125,6 +125,8 @@ def _load():
         "muon_step_batched_profiled": (ctypes.c_int, [ctypes.c_void_p, vpp, vpp, vpp, ctypes.POINTER(HParams),
                                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                                       vpp, ctypes.c_int32]),
+        "muon_step_batched_noalloc": (ctypes.c_int, [ctypes.c_void_p, vpp, vpp, vpp, ctypes.POINTER(HParams),
+                                                     ctypes.c_void_p]),
         "muon_step_event_count": (ctypes.c_int32, [ctypes.c_int32]),
         "dmuon_events_create": (ctypes.c_int, [ctypes.c_int32, vpp]),
         "dmuon_events_elapsed_ms": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
@@ -364,6 +366,35 @@ def muon_step_batched(plan: Plan, grads: Sequence[torch.Tensor], momenta: Sequen
     _check(st, "muon_step_batched")
 
 
+# Bytes of the static device array muon_step_batched_noalloc uses as its
+# workspace (DMUON_NOALLOC_SCRATCH_BYTES in the C header).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def muon_step_batched_noalloc(plan: Plan, grads: Sequence[torch.Tensor], momenta: Sequence[torch.Tensor],
+                              params: Sequence[torch.Tensor], *, lr: float = 0.02, beta: float = 0.95,
+                              weight_decay: float = 0.0, eps: float = 1e-7,
+                              a: float = 3.4445, b: float = -4.7750, c: float = 2.0315, ns_steps: int = 5,
+                              nesterov: bool = True, stream=None) -> None:
+    """muon_step_batched without a workspace argument and without any
+    allocation: the library's static per-GPU scratch array serves as the
+    workspace, so the plan may need at most NOALLOC_SCRATCH_BYTES.  Calls on
+    one GPU share that array and must not overlap in time."""
+    _check_tensors(plan, grads, "grads", "grad")
+    _check_tensors(plan, momenta, "momenta", "momentum")
+    _check_tensors(plan, params, "params", "param")
+    need = plan.workspace_bytes()
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"the plan needs {need} bytes of workspace; muon_step_batched_noalloc holds "
+                         f"{NOALLOC_SCRATCH_BYTES} (use muon_step_batched with a workspace)")
+    hp = HParams(lr, beta, weight_decay, eps, a, b, c, int(ns_steps), 1 if nesterov else 0)
+    g, m, p = _ptr_array(grads), _ptr_array(momenta), _ptr_array(params)
+    vp = ctypes.POINTER(ctypes.c_void_p)
+    st = _lib.muon_step_batched_noalloc(plan.handle, ctypes.cast(g, vp), ctypes.cast(m, vp), ctypes.cast(p, vp),
+                                        ctypes.byref(hp), _stream_handle(stream))
+    _check(st, "muon_step_batched_noalloc")
+
+
 def ns_orthogonalize_batched(plan: Plan, inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor],
                              *, ns_steps: int = 5, a: float = 3.4445, b: float = -4.7750,
                              c: float = 2.0315, eps: float = 1e-7, workspace: torch.Tensor = None,
@@ -563,6 +594,7 @@ class MuonBatch:
 
 __all__ = ["Plan", "PlanEntry", "BucketEntry", "MuonBatch", "DMuonError", "PhaseEvents", "muon_plan",
            "plan_for", "workspace_for", "muon_step_batched", "muon_step_batched_profiled",
+           "muon_step_batched_noalloc", "NOALLOC_SCRATCH_BYTES",
            "ns_orthogonalize_batched", "status_string",
            "version", "library_path", "DMUON_F32", "DMUON_BF16", "ALGO_AUTO", "ALGO_SHORT_SIDE",
            "ALGO_GRAM_SPACE", "PlanOpts", "TuneEntry", "XCD_REMAP_DEFAULT", "autotune", "device_key",

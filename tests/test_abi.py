@@ -27,12 +27,38 @@ def test_exports_every_declared_symbol():
                           "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_bucket_config",
                           "muon_plan_bucket_resident",
                           "muon_autotune_workspace_bytes", "muon_autotune", "muon_plan_destroy",
-                          "muon_step_batched",
+                          "muon_step_batched", "muon_step_batched_noalloc",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
                           "adamw_step_batched", "dmuon_status_string", "dmuon_version"}
     for n in names:
         assert hasattr(raw, n), n
+
+
+def test_noalloc_scratch_size_matches_header():
+    # the binding's copy of the static scratch size is the header's
+    import re
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(os.path.join(root, "include", "dmuon_ns.h")) as f:
+        m = re.search(r"#define DMUON_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == d.NOALLOC_SCRATCH_BYTES
+
+
+@host_only
+def test_noalloc_host_errors_before_device_work():
+    # size and null checks come before any HIP call (fake addresses never dereferenced)
+    hp = d.HParams(0.02, 0.95, 0.0, 1e-7, 3.4445, -4.775, 2.0315, 5, 1)
+    big = d.Plan([(4096, 4096, 1, 1)])  # 128 MiB of workspace
+    assert big.workspace_bytes() > d.NOALLOC_SCRATCH_BYTES
+    f = LIB.muon_step_batched_noalloc
+    g = _arr([0x100000])
+    assert f(big.handle, g, _arr([0x200000]), _arr([0x300000]), ctypes.byref(hp), None) == d.DMUON_ERR_WORKSPACE
+    assert f(None, g, g, g, ctypes.byref(hp), None) == d.DMUON_ERR_INVALID_ARG
+    assert f(big.handle, g, g, g, None, None) == d.DMUON_ERR_INVALID_ARG
+    hp_bad = d.HParams(0.02, 0.95, 0.0, 1e-7, 3.4445, -4.775, 2.0315, -1, 1)
+    assert f(big.handle, g, g, g, ctypes.byref(hp_bad), None) == d.DMUON_ERR_INVALID_ARG
+    assert f(d.Plan([]).handle, None, None, None, ctypes.byref(hp), None) == d.DMUON_OK
 
 
 def test_event_count():
