@@ -180,26 +180,27 @@ def test_resident_buckets(ns_steps):
 
 # More buckets than one grouped launch's segment table holds (24): 30 bf16 shapes
 # that pad to 30 distinct (m, n) buckets, wide and tall alternating, so every
-# phase of the 256-tile class goes out as two launches; both forms of the
-# recurrence run (near-square buckets stay on the short side), and 26 fp32
-# shapes do the same for the fp32 class.
+# phase of the 256-tile class goes out as two launches, in either form of the
+# recurrence (the default keeps these short sides below 1024 on the short side;
+# the Gram space is forced on all of them once), and 26 fp32 shapes do the same
+# for the fp32 class.
 MANY_BF16 = [((m, n) if k % 2 == 0 else (n, m))
              for k, (m, n) in enumerate((m, n_pad - 37) for m, base in ((140, 256), (300, 512), (520, 768))
                                         for n_pad in range(base, base + 2560, 256))]
 MANY_F32 = [(m, m + 64 * j + 5) for m in (40, 100) for j in range(13)]
 
 
-@pytest.mark.parametrize("path", ["bf16", "f32"])
-def test_more_buckets_than_one_launch_holds(path):
+@pytest.mark.parametrize("path,algo", [("bf16", "auto"), ("bf16", "gram_space"), ("f32", "auto")])
+def test_more_buckets_than_one_launch_holds(path, algo):
     shapes = MANY_BF16 if path == "bf16" else MANY_F32
     w = custom_workload(f"many_{path}", shapes, path, "f32")
-    say(f"case {len(shapes)} buckets ({path}) muon_step_batched fp32 zero params")
-    host, out, G, *_ = step_gpu(w, seed=21, zero_params=True)
-    plan = d.plan_for(G, [torch.float32] * len(G))
+    say(f"case {len(shapes)} buckets ({path}, {algo}) muon_step_batched fp32 zero params")
+    host, out, G, *_ = step_gpu(w, seed=21, zero_params=True, algo=algo)
+    plan = d.plan_for(G, [torch.float32] * len(G), algo)
     assert plan.info()[1] == len(shapes) > 24
     if path == "bf16":
         algos = {plan.bucket(b).algo for b in range(plan.info()[1])}
-        assert algos == {d.ALGO_GRAM_SPACE, d.ALGO_SHORT_SIDE}
+        assert algos == {d.ALGO_GRAM_SPACE if algo == "gram_space" else d.ALGO_SHORT_SIDE}
     for i, (r, c) in enumerate(shapes):
         ref = oracle.muon_step(host["G"][i], host["M"][i], host["W"][i], lr=LR, beta=BETA, eps=EPS)
         s_upd = oracle.update_scale(r, c)
@@ -218,6 +219,15 @@ def test_step_shapes(name):
         ref = oracle.muon_step(host["G"][i], host["M"][i], host["W"][i], lr=LR, beta=BETA, eps=EPS)
         assert rel(out["M"][i], ref["M_new"]) < 1e-6, (r, c)
         check_param(out["W"][i], host["W"][i], ref, dt, dt, r, c)
+    # the same gradients and momenta with zero fp32 parameters: W' = -lr s O holds
+    # the step's own O to the path's tolerance (the bf16 W' bound above is dominated
+    # by the parameter's rounding and would admit a much larger O error)
+    say(f"case {name} muon_step_batched fp32 zero params")
+    host, out, *_ = step_gpu(w, seed=5, zero_params=True)
+    for i, (r, c) in enumerate(shapes):
+        ref = oracle.muon_step(host["G"][i], host["M"][i], host["W"][i], lr=LR, beta=BETA, eps=EPS)
+        e = rel(-out["W"][i] / (LR * oracle.update_scale(r, c)), ref["O"])
+        assert e < TOL[dt], ((r, c), e)
 
 
 def test_mixed_precision_batch():
@@ -464,17 +474,36 @@ def test_full_size_step_sampled(wname):
     G, M, W = make_inputs(w, "cuda", seed=0)
     sample = _samples(w)
     host = {i: (f64(G[i]), f64(M[i]), f64(W[i])) for i in sample}
+    M0 = [x.clone() for x in M]
     plan = d.plan_for(G, [x.dtype for x in W])
     ws = d.workspace_for(plan)
     d.muon_step_batched(plan, G, M, W, workspace=ws)
     torch.cuda.synchronize()
+    refs = {}
     for i in sample:
         spec = w.matrices[i]
         say(f"  oracle sample {i} {spec.name} {spec.rows}x{spec.cols}")
-        ref = oracle.muon_step(*host[i], lr=LR, beta=BETA, eps=EPS)
+        refs[i] = ref = oracle.muon_step(*host[i], lr=LR, beta=BETA, eps=EPS)
         assert rel(f64(M[i]), ref["M_new"]) < 1e-6
         check_param(f64(W[i]), host[i][2], ref, "bf16", "bf16", spec.rows, spec.cols)
-    del G, M, W, ws
+    del W, ws
+    # The same step through the same path on the same G and M, with zero fp32
+    # parameters: W' = -lr s O exposes the step's own O, held to 2e-2 per sample
+    # (the bf16 W' bound above is dominated by the parameter's rounding).
+    say(f"case {wname} full muon_step_batched, fp32 zero params")
+    Z = [torch.zeros(x.shape, dtype=torch.float32, device="cuda") for x in G]
+    plan = d.plan_for(G, [torch.float32] * len(G))
+    ws = d.workspace_for(plan)
+    d.muon_step_batched(plan, G, M0, Z, workspace=ws)
+    torch.cuda.synchronize()
+    for i in sample:
+        spec = w.matrices[i]
+        assert torch.equal(M0[i], M[i])
+        O = -f64(Z[i]) / (LR * oracle.update_scale(spec.rows, spec.cols))
+        e = rel(O, refs[i]["O"])
+        say(f"  O through the step, sample {i} {spec.rows}x{spec.cols}: rel err {e:.3e}")
+        assert e < TOL["bf16"]
+    del G, M, M0, Z, ws
     torch.cuda.empty_cache()
 
 

@@ -1,7 +1,8 @@
 """GPU parity on seeded random batches: each batch mixes ragged, tall, wide and
 square matrices, repeated shapes (buckets of several members), both paths
 (bf16 and fp32 gradients), both parameter dtypes, a random iteration count and
-the recurrence form picked automatically or forced to the short side.  One
+the recurrence form picked automatically (the Gram space on buckets of short
+side >= 1024 with n >= 3 m) or forced to the short side.  One
 fused muon_step_batched per batch, compared with the fp64 oracle matrix by
 matrix.
 
@@ -49,8 +50,12 @@ def draw_batch(seed):
     rng = np.random.default_rng(1000 + seed)
     shapes = []
     for _ in range(int(rng.integers(3, 9))):
-        kind = rng.integers(0, 4)
-        if kind == 0:      # small and ragged
+        kind = rng.integers(0, 5)
+        if kind == 4:      # short side >= 1000 and n >= 3 m: the default's Gram-space buckets
+            r = int(rng.integers(1000, 1300))
+            c = int(r * rng.uniform(3.0, 4.0))
+            r, c = (r, c) if rng.integers(0, 2) else (c, r)
+        elif kind == 0:    # small and ragged
             r, c = int(rng.integers(1, 200)), int(rng.integers(1, 200))
         elif kind == 1:    # wide, several tiles
             r = int(rng.integers(64, 600))
