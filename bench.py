@@ -8,15 +8,17 @@ parameter update, with every input already resident in device memory.  The
 default workload is the Llama-3.1-8B projection set's owner share (one of 8 LPT
 owners: 28 matrices, bf16 gradients and parameters, fp32 momentum).
 
-Printed: one JSON line.  ``value`` is the algorithmic Newton-Schulz throughput
-of the whole step: the short-side recurrence's flops, summed over matrices as
-5 (m(m+1)n + m(m+1)m + 2 m^2 n) (the Gram and A A^T triangles plus the dense
-B X product), divided by the step time -- a fixed amount of work per workload,
-so ``value`` moves with 1 / step time whichever form of the recurrence runs.
-``executed_tflops`` and ``pct_bf16_peak`` count the flops the library actually
-performs (fewer for buckets that run the Gram-space form: 6 m^2 n + 14 m^3
-over 5 iterations with a restart after 3, 9 m^2 n + 11 m^3 with restarts every
-2, triangles halved), i.e. the matrix-core utilisation.
+Printed: one JSON line.  ``value`` is the Newton-Schulz throughput of the
+whole step in the flops its kernels execute: the short-side recurrence's
+5 (m(m+1)n + m(m+1)m + 2 m^2 n) per matrix (the Gram and A A^T triangles plus
+the dense B X product), or, for buckets that run the Gram-space form, that
+form's 6 m^2 n + 14 m^3 over 5 iterations with a restart after 3
+(9 m^2 n + 11 m^3 with restarts every 2), triangles halved -- divided by the
+step time.  ``pct_bf16_peak`` is ``value`` over the 2.5 PFLOP/s bf16 dense
+peak, the matrix-core utilisation of the step.  ``effective_tflops`` counts
+the short-side recurrence's flops for every matrix whichever form runs (a
+fixed amount of work per workload, above what the matrix cores execute when
+the Gram space runs).
 ``roofline`` covers the dominant kernel, the B X product, timed live with HIP
 events at its launch boundaries inside the timed steps.
 ``elementwise`` gives the bandwidth-bound passes of the same steps (prep:
@@ -29,7 +31,11 @@ workloads).  ``step_ms_median`` and ``step_ms_min`` are the steps' device
 times from their first to their last event.  ``torch_baseline`` times the same
 step written with PyTorch matrix products (hipBLASLt) on the same inputs, for
 context.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
-the same workload.
+the same workload (one matrix per distinct shape and orientation) and
+extrapolates it to the whole set by multiplicity, with single-thread oracle
+times of the two small workloads.  ``small_workloads`` gives those two
+workloads' graph-replayed step times on the GPU.  ``clock`` samples the shader
+clock and the socket power through amdsmi during the timed steps.
 """
 
 from __future__ import annotations
@@ -125,29 +131,166 @@ def read_traffic(kernel_tag: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, host_samples):
-    """Time the fp64 oracle on a bounded sample of the workload."""
-    import oracle
-
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    flops = 0
-    t0 = time.perf_counter()
-    names = []
+        return len(os.sched_getaffinity(0))
+
+
+def multiplicity(w):
+    """Count of each distinct (rows, cols) of a workload, in first-appearance order."""
+    mult = {}
+    for s in w.matrices:
+        mult[(s.rows, s.cols)] = mult.get((s.rows, s.cols), 0) + 1
+    return mult
+
+
+def cpu_baseline(w, host_samples, gpu_ms_per_step):
+    """Time the fp64 oracle (a dense Muon step per matrix, numpy on the host's
+    BLAS threads) on one matrix per distinct (rows, cols) of the workload, and
+    extrapolate to the whole set by multiplicity."""
+    import oracle
+
+    cores = _blas_threads()
+    mult = multiplicity(w)
+    alg = dense = 0
+    per_shape = {}
+    t_all = time.perf_counter()
     for i, (g, mm, ww) in host_samples:
         spec = w.matrices[i]
+        t0 = time.perf_counter()
         oracle.muon_step(g, mm, ww, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS)
+        per_shape[(spec.rows, spec.cols)] = time.perf_counter() - t0
         m, n = min(spec.rows, spec.cols), max(spec.rows, spec.cols)
-        flops += NS_STEPS * algorithmic_flops(m, n)
-        names.append(f"{spec.name} {spec.rows}x{spec.cols}")
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": "full fp64 oracle Muon step on " + ", ".join(names) + f" ({dt:.1f} s)",
-            "seconds": dt}
+        alg += NS_STEPS * algorithmic_flops(m, n)
+        dense += NS_STEPS * dense_flops(m, n)
+    dt = time.perf_counter() - t_all
+    out = {"value": dense / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": "full fp64 oracle Muon step (numpy, dense products) on one matrix per distinct shape: "
+                     + ", ".join(f"{r}x{c}" for r, c in per_shape) + f" ({dt:.1f} s)",
+           "seconds": round(dt, 3),
+           "value_counts": "flops the oracle executes: dense 4 m^2 n + 2 m^3 per iteration",
+           "oracle_dense_flops_sample": dense,
+           "effective_tflops": round(alg / dt / 1e12, 4)}
+    if set(per_shape) == set(mult):
+        whole = sum(per_shape[k] * mult[k] for k in mult)
+        out["whole_set_seconds_extrapolated"] = round(whole, 2)
+        out["extrapolation"] = ("sum over distinct (rows, cols) of the timed matrix's seconds times its "
+                                "multiplicity: " + ", ".join(f"{r}x{c} x{mult[(r, c)]}" for r, c in mult))
+        out["gpu_speedup_vs_oracle"] = round(whole / (gpu_ms_per_step / 1e3), 1)
+    return out
+
+
+def small_workloads(d, dev, reps: int = 200, oracle_single_thread: bool = True):
+    """The two small workloads (the fp32 256 x 512 matrix and the 96-matrix bf16
+    batch): graph-replayed GPU step time and matrices/s, and the oracle's time
+    for the same step on one host thread."""
+    import torch
+
+    from matrix_optimizer_02_amd.workloads import get_workload, make_inputs
+
+    out = {}
+    for name in ("f32_256x512", "bf16_small_batch_96"):
+        w = get_workload(name)
+        G, M, W = make_inputs(w, dev, seed=0)
+        host = ([(g.double().cpu().numpy(), m.double().cpu().numpy(), x.double().cpu().numpy())
+                 for g, m, x in zip(G, M, W)] if oracle_single_thread else None)
+        plan = d.plan_for(G, [x.dtype for x in W])
+        ws = d.workspace_for(plan, dev)
+        for _ in range(3):
+            d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
+        torch.cuda.synchronize()
+        gr = graph_bench(d, plan, G, M, W, ws, reps, w.count)
+        rec = {"matrices": w.count, "graph_us_per_step": round(gr["ms_per_step"] * 1e3, 2),
+               "matrices_per_s": gr["matrices_per_s"]}
+        if host is not None:
+            import oracle
+            from threadpoolctl import threadpool_limits
+
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                for g, m, x in host:
+                    oracle.muon_step(g, m, x, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS)
+                dt = time.perf_counter() - t0
+            rec["oracle_single_thread_s"] = round(dt, 4)
+            rec["gpu_speedup_vs_oracle_single_thread"] = round(dt / (gr["ms_per_step"] / 1e3), 1)
+        out[name] = rec
+        del G, M, W, ws
+    return out
+
+
+class ClockSampler:
+    """Samples the shader clock and the socket power through amdsmi (the GPU
+    metrics table the driver refreshes) on a host thread, every ``period``
+    seconds between start() and stop().  Records nothing but an error string
+    where amdsmi is unavailable."""
+
+    def __init__(self, period: float = 0.005):
+        self.period = period
+        self.samples = []
+        self.error = None
+        self._thread = None
+        self._stop = None
+        self._h = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self.perf_level = str(amdsmi.amdsmi_get_gpu_perf_level(self._h))
+        except Exception as e:  # pragma: no cover - depends on the box
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        return {"t": time.perf_counter(), "gfxclk": clks, "avg_gfxclk": m.get("average_gfxclk_frequency"),
+                "power": m.get("current_socket_power"), "avg_power": m.get("average_socket_power")}
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+
+        if self._h is None:
+            return
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if self._h is None or not self.samples:
+            return {"source": "amdsmi gpu metrics", "error": self.error or "no samples"}
+        clk = [sum(s["gfxclk"]) / len(s["gfxclk"]) for s in self.samples if s["gfxclk"]]
+        pw = [s["power"] for s in self.samples if isinstance(s["power"], (int, float)) and 0 < s["power"] < 10000]
+        stat = lambda v: ({"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v)} if v else None)
+        try:
+            self._amdsmi.amdsmi_shut_down()
+        except Exception:  # pragma: no cover
+            pass
+        return {"source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, current_socket_power), "
+                          f"sampled every {self.period * 1e3:.0f} ms during the timed steps",
+                "samples": len(self.samples), "sclk_mhz": stat(clk), "socket_power_w": stat(pw),
+                "perf_level": getattr(self, "perf_level", None),
+                "bf16_peak_at_mean_sclk_tflops": (round(BF16_PEAK_TFLOPS * (sum(clk) / len(clk)) / 2400.0, 1)
+                                                  if clk else None),
+                "error": self.error}
 
 
 def graph_bench(d, plan, G, M, W, ws, reps: int, count: int):
@@ -249,6 +392,8 @@ def main(argv=None):
     ap.add_argument("--no-torch-baseline", action="store_true",
                     help="skip timing the same step written with PyTorch matrix products")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-small-workloads", action="store_true",
+                    help="skip the two small workloads' graph-replayed step times")
     ap.add_argument("--tuning-cache", default=None, metavar="PATH",
                     help="run the plan with per-shape tuning entries: loaded from PATH for this device, "
                          "or measured with muon_autotune on the benchmark inputs and saved there")
@@ -286,10 +431,11 @@ def main(argv=None):
     G, M, W = make_inputs(w, dev, seed=args.seed)
     paths = {s.grad_dtype for s in w.matrices}
 
-    # bounded oracle sample: one matrix per distinct shape, smallest first, up to ~8 TFLOP dense
+    # bounded oracle sample: one matrix per distinct (rows, cols), smallest first, up to ~14 TFLOP
+    # dense (about 25 s on 16 host threads)
     host_samples = []
     if not args.no_cpu_baseline:
-        seen, budget = set(), 8e12
+        seen, budget = set(), 14e12
         order = sorted(range(w.count), key=lambda i: dense_flops(min(w.matrices[i].rows, w.matrices[i].cols),
                                                                  max(w.matrices[i].rows, w.matrices[i].cols)))
         for i in order:
@@ -321,13 +467,16 @@ def main(argv=None):
     for _ in range(args.warmup):
         d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
     events = [d.PhaseEvents(NS_STEPS) for _ in range(args.steps)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     for k in range(args.steps):
         d.muon_step_batched_profiled(plan, G, M, W, events[k], lr=LR, beta=BETA, eps=EPS,
                                      workspace=ws, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     names = events[0].names()
@@ -355,7 +504,7 @@ def main(argv=None):
                 execd[k] += v
     executed = sum(execd.values()) + res_flops
     step_s = ms_per_step / 1e3
-    value = alg / step_s / 1e12
+    value = executed / step_s / 1e12
     f32_only = paths == {"f32"}
     peak = FP32_PEAK_TFLOPS if f32_only else BF16_PEAK_TFLOPS
     phase_tot = {k: sum(p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) == k) / len(per)
@@ -384,7 +533,10 @@ def main(argv=None):
         "data": "synthetic (seeded normal gradients, momenta and parameters)",
         "config": {"workload": w.name, "matrices": w.count, "elements": w.elements(),
                    "ns_steps": NS_STEPS, "lr": LR, "beta": BETA, "nesterov": True},
-        "executed_tflops": round(executed / step_s / 1e12, 3),
+        "value_counts": "flops the kernels execute (Gram-space buckets: that form's products; triangles halved)",
+        "executed_flops_per_step": executed,
+        "effective_tflops": round(alg / step_s / 1e12, 3),
+        "effective_flops_per_step": alg,
         "pct_bf16_peak": round(100.0 * executed / step_s / 1e12 / BF16_PEAK_TFLOPS, 3),
         "ns_tflops_dense_equiv": round(dense / step_s / 1e12, 3),
         "recurrence": {"gram_space_matrices": sum(gram_space), "short_side_matrices": w.count - sum(gram_space),
@@ -428,8 +580,11 @@ def main(argv=None):
         out["torch_baseline"] = tb
     if not args.no_adamw:
         out["adamw"] = adamw_bench(d, dev)
+    out["clock"] = clock.summary()
+    if not args.no_small_workloads and args.workload not in ("f32_256x512", "bf16_small_batch_96"):
+        out["small_workloads"] = small_workloads(d, dev, oracle_single_thread=not args.no_cpu_baseline)
     if host_samples:
-        out["cpu_baseline"] = cpu_baseline(w, host_samples)
+        out["cpu_baseline"] = cpu_baseline(w, host_samples, ms_per_step)
     for e in events:
         e.close()
     print(json.dumps(out), flush=True)
