@@ -117,11 +117,12 @@ struct SegSpec {
 };
 
 // One grouped launch per tile class over the given products of one phase.
-hipError_t launch_segs(char* ws, const float* scale, const StepParams& sp, int phase,
+hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const StepParams& sp, int phase,
                        const std::vector<SegSpec>& segs, hipStream_t stream) {
     for (const TileClass& tc : kClasses) {
         GemmArgs ga{};
         ga.ws = ws;
+        ga.queue = queue;
         ga.scale = scale;
         ga.a = sp.a;
         ga.b = sp.b;
@@ -217,6 +218,7 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     DevMatRec* table = reinterpret_cast<DevMatRec*>(ws + p->off_records);
     float* scale = reinterpret_cast<float*>(ws + p->off_scale);
     float* partials = reinterpret_cast<float*>(ws + p->off_partials);
+    uint32_t* queue = reinterpret_cast<uint32_t*>(ws + p->off_queue);
     const int steps = sp.ns_steps;
     const size_t nb = p->buckets.size();
     std::vector<int32_t> seg(nb);
@@ -244,6 +246,7 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     // per-matrix records, plan order, written into the workspace by small launches
     RecChunk chunk{};
     chunk.table = table;
+    chunk.queue = queue;
     int64_t prep_blocks = 0, apply_blocks = 0;
     for (int32_t pi = 0; pi < count; ++pi) {
         const int32_t in = p->order[pi];
@@ -317,7 +320,7 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         return (int64_t)(copy == 0 ? p->buckets[b].off_x0 : p->buckets[b].off_x1);
     };
     auto phase_done = [&](int phase) -> bool {
-        const bool ok = launch_segs(ws, scale, sp, phase, segs, stream) == hipSuccess;
+        const bool ok = launch_segs(ws, queue, scale, sp, phase, segs, stream) == hipSuccess;
         segs.clear();
         return ok;
     };

@@ -63,6 +63,11 @@ constexpr int64_t kMaxBf16Side = int64_t(1) << 27;
 
 inline std::size_t align_up(std::size_t x, std::size_t a = kAlign) { return (x + a - 1) / a * a; }
 
+// The persistent bf16 product launches take tiles from one queue per XCD: a
+// counter per XCD and a count of finished workgroups (the last one resets all
+// of them for the next launch), in the workspace.
+constexpr int kQueueWords = 16;
+
 struct MatPlan {
     int64_t rows, cols;
     int32_t grad_dtype, param_dtype;
@@ -106,7 +111,9 @@ struct dmuon_plan {
     std::vector<dmuon::BucketPlan> buckets;  // execution order
     std::vector<int32_t> order;              // plan index -> input index
     int64_t total_prep_tiles = 0;
-    std::size_t off_records = 0, off_scale = 0, off_partials = 0;
+    // off_queue: the grouped launches' tile-queue counters (dmuon::kQueueWords
+    // uint32), zeroed at the start of every call
+    std::size_t off_records = 0, off_scale = 0, off_partials = 0, off_queue = 0;
     std::size_t workspace_bytes = 0;
 };
 

@@ -27,6 +27,7 @@ constexpr int kThreads = 256;
 __global__ void write_records_kernel(RecChunk c) {
     const int i = threadIdx.x;
     if (i < c.n) c.table[c.first + i] = c.rec[i];
+    if (c.first == 0 && i < kQueueWords) c.queue[i] = 0u;  // the call's tile queues start empty
 }
 
 // Sum of squares of four values, in one fixed order of explicit operations.

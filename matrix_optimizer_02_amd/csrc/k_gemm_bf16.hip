@@ -21,6 +21,10 @@
 // "Benutting van Symmetrie"); matrices of similar shapes run jointly to keep
 // the GPU occupied and amortise dispatch (same section, "Batching").
 //
+// Each launch is persistent: one workgroup per CU (two for T = 128) takes
+// tiles from its XCD's queue until none is left, and the next tile's first
+// slab loads while the current tile's output is written (see the kernel).
+//
 // Tile: T x T outputs per workgroup (T = 256 or 128).  T = 256: 8 waves in a
 // 2 x 4 grid, two per SIMD, each 128 x 64 outputs as 4 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16 (128 accumulator registers, so two waves fit a
@@ -91,9 +95,10 @@ struct TileCfg {
     static constexpr int kPRowBytes = 2 * T;
     static constexpr int kPChunks = kPRowBytes / 16;
     static constexpr int kPDmaRows = 1024 / kPRowBytes;
-    // epilogue tile: T rows of T bf16
+    // epilogue tile: T rows of T bf16, staged through one stage in kEHalves pieces
     static constexpr int kERowBytes = 2 * T;
     static constexpr int kEChunks = T / 8;
+    static constexpr int kEHalves = T * kERowBytes / kStageBytes;
 };
 
 // Wait until at most N of the wave's vector-memory loads are in flight (loads
@@ -141,60 +146,93 @@ __device__ __forceinline__ int swizzle_p(int r) { return (0xEA40 >> ((r & 3) * 4
 template <int T>
 __device__ __forceinline__ int swizzle_e(int r) { return r & (T / 8 - 1); }
 
+// A tile of a launch: segment, matrix slot and output tile (I, J).
+struct TileInfo {
+    int s, slot, I, J;
+};
+
+// Where a tile's slabs come from: wave-uniform bases and strides (every side
+// is below 2^27 elements, so strides and K fit 32 bits), and each lane's
+// 32-bit offsets (two, by load parity).
+struct LoadPlan {
+    const char* p_base;
+    const char* q_base;
+    int32_t p_k, p_q, q_q, k_rot, K;
+    uint32_t voff_p[2], voff_q[2];
+};
+
+// Persistent: each workgroup computes tiles until its XCD's queue is empty.
+// The launch's tiles are dealt to the XCDs exactly as a grid of one
+// workgroup per tile would deal them (xcd_map of block ids x, x + 8, x + 16,
+// ... to XCD x; the hardware places block b on XCD b % 8).  The k-th
+// workgroup of XCD x starts with that XCD's k-th tile and then takes the next
+// untaken one, counted by the XCD's counter (so tiles of one XCD run in
+// their dealt order, longest segments first).  Consecutive tiles of a
+// workgroup overlap: the last slab of a tile loads the next tile's first
+// slab into the stage it has finished with, and the epilogue stages the
+// output through the other stage, so the next tile's loads are in flight
+// while the output is written, and its stores drain while the next tile
+// runs.  Every output element is still accumulated by one wave in one k
+// order, so results do not depend on which workgroup takes which tile.
 template <int T, int PHASE>
 __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
-    static_assert(2 * C::kStageBytes >= T * C::kERowBytes, "epilogue tile fits the stages");
-
-    // ---- which tile of which matrix --------------------------------------------
-    int s, local;
-    xcd_map((int)blockIdx.x, args.nseg, [&](int i) { return args.seg[i].count * args.seg[i].tiles_per_mat; },
-            [&](int i) { return args.seg[i].first_block; }, [&](int i) { return args.seg[i].xcd_remap != 0; },
-            s, local);
-    const GemmSeg& sg = args.seg[s];
-    const int slot = local / sg.tiles_per_mat;
-    const int t = local - slot * sg.tiles_per_mat;
-    const int plan_idx = sg.plan_base + slot;
-
-    int I, J;  // tile coordinates in the output (row tile, column tile)
-    const uint16_t *P, *Q;
-    int64_t ldq;  // leading dimension of Q's rows (= K extent)
-    if (PHASE == kBX) {
-        if (DMUON_BANDED) {
-            bx_decode_banded(t, sg.tn, sg.tm, I, J);  // I: long-side tile, J: short-side tile
-        } else {
-            I = t / sg.tm;
-            J = t - I * sg.tm;
-        }
-        P = reinterpret_cast<const uint16_t*>(args.ws + sg.p_off + slot * sg.x_stride);  // X: m x n
-        Q = reinterpret_cast<const uint16_t*>(args.ws + sg.q_off + slot * sg.a_stride);
-        ldq = sg.m_pad;
-    } else {
-        if (DMUON_BANDED) {
-            tri_decode_banded(t, sg.tm, I, J);
-        } else {
-            int tt = t, i = 0;
-            while (tt >= sg.tm - i) {
-                tt -= sg.tm - i;
-                ++i;
-            }
-            I = i;
-            J = i + tt;
-        }
-        P = reinterpret_cast<const uint16_t*>(args.ws + sg.p_off +
-                                              slot * (PHASE == kGram ? sg.x_stride : sg.a_stride));
-        Q = PHASE == kProd ? reinterpret_cast<const uint16_t*>(args.ws + sg.q_off + slot * sg.a_stride) : P;
-        ldq = PHASE == kGram ? sg.n_pad : sg.m_pad;
-    }
-    const int64_t K = ldq;
-    const uint16_t* Qt = Q + (int64_t)J * T * ldq;
+    __shared__ int s_next;  // queue position of this workgroup's next tile
+    static_assert(C::kEHalves * C::kStageBytes == T * C::kERowBytes, "epilogue pieces fill one stage each");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wr = wave / C::WC, wc = wave % C::WC;
 
-    // ---- global -> LDS (direct) ----------------------------------------------------
+    // ---- this workgroup's queue ------------------------------------------------------
+    const int x = (int)(blockIdx.x % kXcds);
+    const int wgs_x = ((int)gridDim.x - x + kXcds - 1) / kXcds;  // workgroups on XCD x
+    const int total = args.total_blocks;
+    const int count_x = total > x ? (total - x + kXcds - 1) / kXcds : 0;  // tiles dealt to XCD x
+
+    auto decode = [&](int kq, TileInfo& ti) {
+        int local;
+        xcd_map(x + kXcds * kq, args.nseg, [&](int i) { return args.seg[i].count * args.seg[i].tiles_per_mat; },
+                [&](int i) { return args.seg[i].first_block; }, [&](int i) { return args.seg[i].xcd_remap != 0; },
+                ti.s, local);
+        const GemmSeg& sg = args.seg[ti.s];
+        ti.slot = local / sg.tiles_per_mat;
+        const int t = local - ti.slot * sg.tiles_per_mat;
+        if (PHASE == kBX) {
+            if (DMUON_BANDED) {
+                bx_decode_banded(t, sg.tn, sg.tm, ti.I, ti.J);  // I: long-side tile, J: short-side tile
+            } else {
+                ti.I = t / sg.tm;
+                ti.J = t - ti.I * sg.tm;
+            }
+        } else {
+            if (DMUON_BANDED) {
+                tri_decode_banded(t, sg.tm, ti.I, ti.J);
+            } else {
+                int tt = t, i = 0;
+                while (tt >= sg.tm - i) {
+                    tt -= sg.tm - i;
+                    ++i;
+                }
+                ti.I = i;
+                ti.J = i + tt;
+            }
+        }
+    };
+    // The P operand (B X: X, read k-major) of a tile's matrix, and the leading
+    // dimension of the K-contiguous rows (Q's, and P's outside B X): the K extent.
+    auto operand_p = [&](const TileInfo& ti) -> const uint16_t* {
+        const GemmSeg& sg = args.seg[ti.s];
+        return reinterpret_cast<const uint16_t*>(
+            args.ws + sg.p_off + ti.slot * (PHASE == kBX || PHASE == kGram ? sg.x_stride : sg.a_stride));
+    };
+    auto k_extent = [&](const TileInfo& ti) -> int32_t {
+        const GemmSeg& sg = args.seg[ti.s];
+        return (int32_t)(PHASE == kGram ? sg.n_pad : sg.m_pad);
+    };
+
+    // ---- global -> LDS (direct) ------------------------------------------------------
     // One global_load_lds_dwordx4 of a wave fills 1 KB of LDS: lane l writes
     // bytes 16 l .. 16 l + 15 of it, so it fetches the global chunk that the
     // swizzle places there.  Load q (= wave kDmaPerOp + i) of an operand slab
@@ -207,45 +245,56 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     //   B X P slab (rows k of X): R = 2 (T = 256) or 4, chunk swizzle
     //   swizzle_p of the row, whose two low bits hold 2 (q & 1) + l / 32 or l / 16.
     static_assert(C::kDmaPerOp % 2 == 0, "load parity");
-    const int64_t p_row_ld = PHASE == kBX ? sg.n_pad : ldq;  // P slab row stride (elements)
-    uint32_t voff_p[2], voff_q[2];
-    #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        if (PHASE == kBX) {
-            const int row = C::kPDmaRows * par + lane / C::kPChunks;
-            const int lc = (lane % C::kPChunks) ^ swizzle_p(row);
-            voff_p[par] = (uint32_t)(2 * ((lane / C::kPChunks) * p_row_ld + lc * 8));
-        } else {
+    auto plan_loads = [&](const TileInfo& ti, LoadPlan& lp) {
+        const GemmSeg& sg = args.seg[ti.s];
+        const int32_t ldq = k_extent(ti);
+        const int32_t p_row_ld = PHASE == kBX ? (int32_t)sg.n_pad : ldq;  // P slab row stride (elements)
+        const uint16_t* P = operand_p(ti);
+        const uint16_t* Q = PHASE == kBX || PHASE == kProd
+                                ? reinterpret_cast<const uint16_t*>(args.ws + sg.q_off + ti.slot * sg.a_stride)
+                                : P;
+        #pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            if (PHASE == kBX) {
+                const int row = C::kPDmaRows * par + lane / C::kPChunks;
+                const int lc = (lane % C::kPChunks) ^ swizzle_p(row);
+                lp.voff_p[par] = (uint32_t)(2 * ((lane / C::kPChunks) * p_row_ld + lc * 8));
+            } else {
+                const int lc = (lane % kChunks) ^ swizzle(kDmaRows * par + lane / kChunks);
+                lp.voff_p[par] = (uint32_t)(2 * ((lane / kChunks) * p_row_ld + lc * 8));
+            }
             const int lc = (lane % kChunks) ^ swizzle(kDmaRows * par + lane / kChunks);
-            voff_p[par] = (uint32_t)(2 * ((lane / kChunks) * p_row_ld + lc * 8));
+            lp.voff_q[par] = (uint32_t)(2 * ((lane / kChunks) * ldq + lc * 8));
         }
-        const int lc = (lane % kChunks) ^ swizzle(kDmaRows * par + lane / kChunks);
-        voff_q[par] = (uint32_t)(2 * ((lane / kChunks) * ldq + lc * 8));
-    }
-    // wave-uniform byte addresses: P slab at k0 = p_base + k0 p_k + q p_q
-    const char* p_base = reinterpret_cast<const char*>(P) + (PHASE == kBX ? 2 * (int64_t)I * T : 2 * (int64_t)I * T * ldq);
-    const char* q_base = reinterpret_cast<const char*>(Qt);
-    const int64_t p_k = PHASE == kBX ? 2 * sg.n_pad : 2, p_q = PHASE == kBX ? 2 * C::kPDmaRows * sg.n_pad : 16 * ldq;
-    const int64_t q_q = 16 * ldq;
-    // The square's K loop starts right after the T-wide k range that its
-    // epilogue reads back (A columns I T .., the mirrored A block), so that
-    // range is loaded last and the epilogue finds it in L2.  K is a multiple
-    // of T.
-    int64_t k_rot = 0;
-    if (DMUON_ROTATE_K && PHASE == kSquare) {
-        k_rot = (int64_t)(I + 1) * T;
-        if (k_rot >= K) k_rot -= K;
-    }
+        // wave-uniform byte addresses: P slab at k0 = p_base + k0 p_k + q p_q
+        lp.p_base = reinterpret_cast<const char*>(P) +
+                    (PHASE == kBX ? 2 * (int64_t)ti.I * T : 2 * (int64_t)ti.I * T * ldq);
+        lp.q_base = reinterpret_cast<const char*>(Q + (int64_t)ti.J * T * ldq);
+        lp.p_k = PHASE == kBX ? 2 * (int32_t)sg.n_pad : 2;
+        lp.p_q = PHASE == kBX ? 2 * C::kPDmaRows * (int32_t)sg.n_pad : 16 * ldq;
+        lp.q_q = 16 * ldq;
+        lp.K = ldq;
+        // The square's K loop starts right after the T-wide k range that its
+        // epilogue reads back (A columns I T .., the mirrored A block), so that
+        // range is loaded last and the epilogue finds it in L2.  K is a multiple
+        // of T.
+        lp.k_rot = 0;
+        if (DMUON_ROTATE_K && PHASE == kSquare) {
+            lp.k_rot = (ti.I + 1) * T;
+            if (lp.k_rot >= lp.K) lp.k_rot -= lp.K;
+        }
+    };
     // Loads i0 .. i1-1 (of kDmaPerOp per operand) of the slab at loop position
-    // k0 into the stage at dst.
-    auto dma_part = [&](int64_t k0, char* dst, int i0, int i1) {
-        k0 += k_rot;
-        if (k0 >= K) k0 -= K;
+    // k0 of the tile lp describes into the stage at dst.
+    auto dma_part = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+        k0 += lp.k_rot;
+        if (k0 >= lp.K) k0 -= lp.K;
         #pragma unroll
         for (int i = i0; i < i1; ++i) {
             const int q = wave * C::kDmaPerOp + i;  // 1 KB block of the operand slab
-            dma16(p_base + k0 * p_k + q * p_q, voff_p[i & 1], lds_offset(dst + q * 1024));
-            dma16(q_base + 2 * k0 + q * q_q, voff_q[i & 1], lds_offset(dst + C::kOperandBytes + q * 1024));
+            dma16(lp.p_base + (int64_t)k0 * lp.p_k + (int64_t)q * lp.p_q, lp.voff_p[i & 1], lds_offset(dst + q * 1024));
+            dma16(lp.q_base + 2 * (int64_t)k0 + (int64_t)q * lp.q_q, lp.voff_q[i & 1],
+                  lds_offset(dst + C::kOperandBytes + q * 1024));
         }
     };
     // A slab's loads go out in three pieces: the first right after the barrier
@@ -256,13 +305,6 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     constexpr int kPiece2 = DMUON_SPREAD ? (C::kPiece2Eighths * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
 
     floatx16 acc[C::FI][C::FJ];
-    #pragma unroll
-    for (int i = 0; i < C::FI; ++i)
-        #pragma unroll
-        for (int j = 0; j < C::FJ; ++j)
-            #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
     const int lrow = lane & 31, khalf = lane >> 5;
     const int swz = swizzle(lrow);  // fragment rows start at multiples of 32
     const int a_row0 = (wr * C::RW + lrow) * kRowBytes;
@@ -333,98 +375,56 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         if ((NV) > NMFMA) __builtin_amdgcn_sched_group_barrier(0x010, (NV) - NMFMA, 0);           \
         __builtin_amdgcn_sched_barrier(0);                                                        \
     } while (0)
-    // Slab KT_ (not the last) from stage CUR: pieces 1 and 2 of slab KT_ + 1
-    // go into stage OTH during the first two k-steps.  The last k-step waits
-    // for slab KT_ + 1 (nothing else is in flight then); the barrier publishes
-    // every wave's share of it and makes sure every wave is done reading CUR,
-    // which then takes the first piece of slab KT_ + 2.
-#define DMUON_SLAB(KT_, CUR, OTH)                                                                 \
+    // The first KS - 1 k-steps of the slab in stage CUR; pieces 1 and 2 of the
+    // slab at k0 = K0_ of the tile LP_ go into stage OTH during the first two.
+#define DMUON_KSTEPS(LP_, K0_, CUR, OTH)                                                          \
     do {                                                                                          \
-        const int64_t knext_ = (int64_t)((KT_) + 1) * kBK;                                        \
         _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                                   \
-            if (ks == 0) dma_part(knext_, OTH, kPiece1, kPiece2);                                 \
-            if (ks == 1) dma_part(knext_, OTH, kPiece2, C::kDmaPerOp);                            \
+            if (ks == 0) dma_part(LP_, K0_, OTH, kPiece1, kPiece2);                               \
+            if (ks == 1) dma_part(LP_, K0_, OTH, kPiece2, C::kDmaPerOp);                          \
             DMUON_READ((ks + 1) & 1, CUR, ks + 1);                                                \
             DMUON_MFMA(ks & 1);                                                                   \
             if (ks == 0) DMUON_INTERLEAVE(NV1);                                                   \
             else if (ks == 1) DMUON_INTERLEAVE(NV2);                                              \
             else DMUON_INTERLEAVE(0);                                                             \
         }                                                                                         \
-        wait_vm<0>();                                                                             \
-        __syncthreads();                                                                          \
-        __builtin_amdgcn_sched_barrier(0);                                                        \
-        if ((KT_) + 2 < KT) dma_part(knext_ + kBK, CUR, 0, kPiece1);                              \
-        __builtin_amdgcn_sched_barrier(0);                                                        \
-        DMUON_READ(0, OTH, 0);                                                                    \
-        DMUON_MFMA((KS - 1) & 1);                                                                 \
-        DMUON_INTERLEAVE(0);                                                                      \
-    } while (0)
-#define DMUON_LAST_SLAB(CUR)                                                                      \
-    do {                                                                                          \
-        _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                                   \
-            DMUON_READ((ks + 1) & 1, CUR, ks + 1);                                                \
-            DMUON_MFMA(ks & 1);                                                                   \
-            DMUON_INTERLEAVE(0);                                                                  \
-        }                                                                                         \
-        DMUON_MFMA((KS - 1) & 1);                                                                 \
     } while (0)
 
-    const int KT = (int)(K / kBK);
-    // prologue: slab 0 whole and the first piece of slab 1; wait for slab 0
-    dma_part(0, smem, 0, C::kDmaPerOp);
-    if (KT > 1) {
-        dma_part(kBK, smem + C::kStageBytes, 0, kPiece1);
-        wait_vm<2 * kPiece1>();
-    } else {
-        wait_vm<0>();
-    }
-    __syncthreads();
-    DMUON_READ(0, smem, 0);
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-        char* cur = smem + (kt & 1) * C::kStageBytes;
-        char* oth = smem + ((kt + 1) & 1) * C::kStageBytes;
-        DMUON_SLAB(kt, cur, oth);
-    }
-    DMUON_LAST_SLAB(smem + ((KT - 1) & 1) * C::kStageBytes);
-#undef DMUON_SLAB
-#undef DMUON_LAST_SLAB
-#undef DMUON_INTERLEAVE
-#undef DMUON_READ
-#undef DMUON_READ_A
-#undef DMUON_MFMA
-
-    // ---- epilogue -----------------------------------------------------------------
+    // ---- epilogue ---------------------------------------------------------------------
     // acc[i][j][v] holds output row  wr*RW + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4
     //                  and column  wc*CW + 32 j + lane % 32   of the T x T tile,
     // i.e. four consecutive rows r0 .. r0 + 3 of one column c per (i, j, v / 4).
     // The tile goes through LDS transposed, as E[c][r] = C[r][c]: each lane's
-    // four values are one 8-byte piece of a row of E.
-    const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
-    // T rows of 2 T bytes from global (row stride ld elements) into E, whole.
-    auto load_tile = [&](const uint16_t* src, int64_t ld) {
-        constexpr int kLoads = T * C::kERowBytes / 1024 / C::NW;  // 1 KB loads per wave
+    // four values are one 8-byte piece of a row of E.  E is staged through one
+    // stage in kEHalves pieces of kERows rows (columns c) each, the waves
+    // holding a piece's columns writing it.
+    constexpr int kERows = T / C::kEHalves;
+    const int my_piece = (wc * C::CW) / kERows;
+    // kERows rows of 2 T bytes from global (row stride ld elements) into E, whole.
+    auto load_piece = [&](int eln, char* ebuf, const uint16_t* src, int64_t ld) {
+        constexpr int kLoads = kERows * C::kERowBytes / 1024 / C::NW;  // 1 KB loads per wave
         #pragma unroll 8
         for (int i = 0; i < kLoads; ++i) {
             const int q = wave * kLoads + i;
-            const int row = (1024 / C::kERowBytes) * q + lane / C::kEChunks;
-            const int lc = (lane % C::kEChunks) ^ swizzle_e<T>(row);
-            dma16(src + row * ld + lc * 8, lds_offset(smem + q * 1024));
+            const int row = (1024 / C::kERowBytes) * q + eln / C::kEChunks;
+            const int lc = (eln % C::kEChunks) ^ swizzle_e<T>(row);
+            dma16(src + row * ld + lc * 8, lds_offset(ebuf + q * 1024));
         }
         wait_vm<0>();
         __syncthreads();
     };
     // E row c, columns r .. r + 3 (r a multiple of 4)
-    auto e_ptr = [&](int c, int r) -> char* {
-        return smem + c * C::kERowBytes + (((r >> 3) ^ swizzle_e<T>(c)) << 4) + (r & 7) * 2;
+    auto e_ptr = [&](char* ebuf, int c, int r) -> char* {
+        return ebuf + c * C::kERowBytes + (((r >> 3) ^ swizzle_e<T>(c)) << 4) + (r & 7) * 2;
     };
     // E rows to global rows (row stride ld elements), whole 16-byte chunks.
-    auto store_rows = [&](uint16_t* dst, int64_t ld) {
-        constexpr int kStores = T * C::kEChunks / C::NT;
+    auto store_rows = [&](int etid, char* ebuf, uint16_t* dst, int64_t ld) {
+        constexpr int kStores = kERows * C::kEChunks / C::NT;
         #pragma unroll 8
         for (int i = 0; i < kStores; ++i) {
-            const int q = tid + C::NT * i;
+            const int q = etid + C::NT * i;
             const int row = q / C::kEChunks, lc = q % C::kEChunks;
-            const uint4 v = *reinterpret_cast<const uint4*>(smem + row * C::kERowBytes +
+            const uint4 v = *reinterpret_cast<const uint4*>(ebuf + row * C::kERowBytes +
                                                             ((lc ^ swizzle_e<T>(row)) << 4));
             *reinterpret_cast<uint4*>(dst + row * ld + lc * 8) = v;
         }
@@ -435,9 +435,9 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     // r0 + 4 q .. + 3) and hands lane i the four values E[c0 .. c0 + 3][r0 + i];
     // two such reads give a lane 8 consecutive c of one r.  A wave covers 16
     // rows r and 32 columns c per store, the 4 groups taking 8 columns each.
-    auto store_cols = [&](uint16_t* dst, int64_t ld) {
-        const int g = lane >> 4, i16 = lane & 15, k = i16 >> 2, q = i16 & 3;
-        constexpr int kRowBlocks = T / 16, kColBlocks = T / 32;
+    auto store_cols = [&](int eln, char* ebuf, uint16_t* dst, int64_t ld) {
+        const int g = eln >> 4, i16 = eln & 15, k = i16 >> 2, q = i16 & 3;
+        constexpr int kRowBlocks = T / 16, kColBlocks = kERows / 32;
         #pragma unroll 4
         for (int it = 0; it < kRowBlocks * kColBlocks / C::NW; ++it) {
             const int w = C::NW * it + wave;
@@ -446,85 +446,225 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
                 h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_shortx4*)((__attribute__((address_space(3))) char*)e_ptr(cb + 4 * hh + k, r0 + 4 * q)));
+                    (lds_shortx4*)((__attribute__((address_space(3))) char*)e_ptr(ebuf, cb + 4 * hh + k, r0 + 4 * q)));
             const shortx8 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
             *reinterpret_cast<shortx8*>(dst + (int64_t)(r0 + i16) * ld + cb) = v;
         }
     };
-
-    __syncthreads();  // every wave is done with the last slab
-    if (PHASE == kBX) {
-        // Tile rows are long-side indices r, columns short-side indices c:
-        // X'[c][r] = s acc[r][c]; E is the X' tile (T rows c, T columns r).
-        const int64_t ldn = sg.n_pad;
-        uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + slot * sg.x_stride) +
-                       (int64_t)J * T * ldn + (int64_t)I * T;
-        #pragma unroll
-        for (int i = 0; i < C::FI; ++i)
+    auto epilogue = [&](const TileInfo& ti, char* ebuf) {
+        // Lane indices passed through an empty asm statement: the epilogue's
+        // per-lane addresses are then computed here, once per tile, rather
+        // than hoisted out of the tile loop into registers the main loop needs.
+        int etid = tid;
+        asm volatile("" : "+v"(etid));
+        const int eln = etid & 63, elrow = eln & 31, ekhalf = eln >> 5;
+        // likewise the segment's fields: loaded here, not kept through the main loop
+        int es = ti.s;
+        asm volatile("" : "+s"(es));
+        const GemmSeg& sg = args.seg[es];
+        const int plan_idx = sg.plan_base + ti.slot;
+        const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
+        if (PHASE == kBX) {
+            // Tile rows are long-side indices r, columns short-side indices c:
+            // X'[c][r] = s acc[r][c]; E is the X' tile (T rows c, T columns r).
+            const int64_t ldn = sg.n_pad;
+            uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + ti.slot * sg.x_stride) +
+                           (int64_t)ti.J * T * ldn + (int64_t)ti.I * T;
             #pragma unroll
-            for (int j = 0; j < C::FJ; ++j)
-                #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * khalf;
-                    const int c = wc * C::CW + j * 32 + lrow;
-                    uint2 o;
-                    o.x = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 0]) |
-                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 1]) << 16);
-                    o.y = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 2]) |
-                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 3]) << 16);
-                    *reinterpret_cast<uint2*>(e_ptr(c, r0)) = o;
-                }
-        __syncthreads();
-        store_rows(Xd, ldn);
-    } else {
-        // Out[I T + r][J T + c] = C[r][c] = E[c][r] and, off the diagonal, the
-        // mirror Out[J T + c][I T + r] = E[c][r].  E's rows are rows of block
-        // (J, I); on the diagonal that block is the tile itself (symmetric).
-        // The square's b A term reads A's block (J, I) = block (I, J)^T into E
-        // first (A is symmetric and stored whole).
-        const int64_t ld = sg.m_pad;
-        uint16_t* Out = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + slot * sg.a_stride);
-        const float alpha = PHASE == kGram ? first_scale * first_scale : PHASE == kSquare ? args.c : 1.0f;
-        const float beta = args.b;
-        if (PHASE == kSquare) load_tile(P + (int64_t)J * T * ld + (int64_t)I * T, ld);
-        #pragma unroll
-        for (int i = 0; i < C::FI; ++i)
-            #pragma unroll
-            for (int j = 0; j < C::FJ; ++j)
-                #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * khalf;
-                    const int c = wc * C::CW + j * 32 + lrow;
-                    char* p = e_ptr(c, r0);
-                    float v[4];
+            for (int h = 0; h < C::kEHalves; ++h) {
+                if (my_piece == h) {
                     #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * v4 + e];
-                    if (PHASE == kSquare) {
-                        const uint2 x = *reinterpret_cast<const uint2*>(p);
-                        v[0] = fmaf(beta, __uint_as_float(x.x << 16), v[0]);
-                        v[1] = fmaf(beta, __uint_as_float(x.x & 0xffff0000u), v[1]);
-                        v[2] = fmaf(beta, __uint_as_float(x.y << 16), v[2]);
-                        v[3] = fmaf(beta, __uint_as_float(x.y & 0xffff0000u), v[3]);
-                        if (I == J) {  // the a I term on the diagonal
+                    for (int i = 0; i < C::FI; ++i)
+                        #pragma unroll
+                        for (int j = 0; j < C::FJ; ++j)
                             #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (r0 + e == c) v[e] += args.a;
-                        }
-                    }
-                    uint2 o;
-                    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(p) = o;
+                            for (int v4 = 0; v4 < 4; ++v4) {
+                                const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * ekhalf;
+                                const int c = wc * C::CW + j * 32 + elrow - h * kERows;
+                                uint2 o;
+                                o.x = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 0]) |
+                                      ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 1]) << 16);
+                                o.y = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 2]) |
+                                      ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 3]) << 16);
+                                *reinterpret_cast<uint2*>(e_ptr(ebuf, c, r0)) = o;
+                            }
                 }
+                if (h == 0) wait_vm<0>();  // the next tile's slab 0, before any store is issued
+                __syncthreads();
+                store_rows(etid, ebuf, Xd + (int64_t)h * kERows * ldn, ldn);
+                if (h + 1 < C::kEHalves) __syncthreads();  // before the next piece overwrites E
+            }
+        } else {
+            // Out[I T + r][J T + c] = C[r][c] = E[c][r] and, off the diagonal, the
+            // mirror Out[J T + c][I T + r] = E[c][r].  E's rows are rows of block
+            // (J, I); on the diagonal that block is the tile itself (symmetric).
+            // The square's b A term reads A's block (J, I) = block (I, J)^T into E
+            // first (A is symmetric and stored whole).
+            const int64_t ld = sg.m_pad;
+            uint16_t* Out = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + ti.slot * sg.a_stride);
+            const float alpha = PHASE == kGram ? first_scale * first_scale : PHASE == kSquare ? args.c : 1.0f;
+            const float beta = args.b;
+            #pragma unroll
+            for (int h = 0; h < C::kEHalves; ++h) {
+                if (PHASE == kSquare)
+                    load_piece(eln, ebuf,
+                               reinterpret_cast<const uint16_t*>(args.ws + sg.p_off + ti.slot * sg.a_stride) +
+                                   ((int64_t)ti.J * T + h * kERows) * ld + (int64_t)ti.I * T,
+                               ld);
+                if (my_piece == h) {
+                    #pragma unroll
+                    for (int i = 0; i < C::FI; ++i)
+                        #pragma unroll
+                        for (int j = 0; j < C::FJ; ++j)
+                            #pragma unroll
+                            for (int v4 = 0; v4 < 4; ++v4) {
+                                const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * ekhalf;
+                                const int cg = wc * C::CW + j * 32 + elrow;  // column in the tile
+                                char* p = e_ptr(ebuf, cg - h * kERows, r0);
+                                float v[4];
+                                #pragma unroll
+                                for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * v4 + e];
+                                if (PHASE == kSquare) {
+                                    const uint2 xa = *reinterpret_cast<const uint2*>(p);
+                                    v[0] = fmaf(beta, __uint_as_float(xa.x << 16), v[0]);
+                                    v[1] = fmaf(beta, __uint_as_float(xa.x & 0xffff0000u), v[1]);
+                                    v[2] = fmaf(beta, __uint_as_float(xa.y << 16), v[2]);
+                                    v[3] = fmaf(beta, __uint_as_float(xa.y & 0xffff0000u), v[3]);
+                                    if (ti.I == ti.J) {  // the a I term on the diagonal
+                                        #pragma unroll
+                                        for (int e = 0; e < 4; ++e)
+                                            if (r0 + e == cg) v[e] += args.a;
+                                    }
+                                }
+                                uint2 o;
+                                o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                                o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                                *reinterpret_cast<uint2*>(p) = o;
+                            }
+                }
+                if (h == 0) wait_vm<0>();  // the next tile's slab 0, before any store is issued
+                __syncthreads();
+                store_rows(etid, ebuf, Out + ((int64_t)ti.J * T + h * kERows) * ld + (int64_t)ti.I * T, ld);
+                if (ti.I != ti.J)
+                    store_cols(eln, ebuf, Out + (int64_t)ti.I * T * ld + (int64_t)ti.J * T + h * kERows, ld);
+                if (h + 1 < C::kEHalves) __syncthreads();  // before the next piece overwrites E
+            }
+        }
+    };
+
+    // ---- the tiles of this workgroup ------------------------------------------------------
+    int kq = (int)(blockIdx.x / kXcds);  // this workgroup's first tile of its XCD's queue
+    if (kq < count_x) {
+        TileInfo cur;
+        decode(kq, cur);
+        LoadPlan L;
+        plan_loads(cur, L);
+        // prologue: slab 0 whole and the first piece of slab 1; wait for slab 0
+        dma_part(L, 0, smem, 0, C::kDmaPerOp);
+        dma_part(L, kBK, smem + C::kStageBytes, 0, kPiece1);
+        wait_vm<2 * kPiece1>();
         __syncthreads();
-        store_rows(Out + (int64_t)J * T * ld + (int64_t)I * T, ld);
-        if (I != J) store_cols(Out + (int64_t)I * T * ld + (int64_t)J * T, ld);
+        int par = 0;  // slab kt of the current tile sits in stage (kt + par) & 1
+        for (;;) {
+            // the queue position of the tile after this one (read once the
+            // atomic has returned, at the penultimate slab)
+            uint32_t taken = 0;
+            if (tid == 0) taken = atomicAdd(args.queue + x, 1u);
+            #pragma unroll
+            for (int i = 0; i < C::FI; ++i)
+                #pragma unroll
+                for (int j = 0; j < C::FJ; ++j)
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            auto stage = [&](int kt) { return smem + ((kt + par) & 1) * C::kStageBytes; };
+            const int KT = (int)(L.K / kBK);  // >= 2: K is a multiple of the tile
+            DMUON_READ(0, stage(0), 0);
+            // Slab kt (not one of the last two): pieces 1 and 2 of slab kt + 1 go
+            // into its stage during the first two k-steps.  The last k-step waits
+            // for slab kt + 1 (nothing else is in flight then); the barrier
+            // publishes every wave's share of it and makes sure every wave is done
+            // reading slab kt's stage, which then takes the first piece of slab kt + 2.
+            for (int kt = 0; kt + 2 < KT; ++kt) {
+                DMUON_KSTEPS(L, (kt + 1) * kBK, stage(kt), stage(kt + 1));
+                wait_vm<0>();
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                dma_part(L, (kt + 2) * kBK, stage(kt), 0, kPiece1);
+                __builtin_amdgcn_sched_barrier(0);
+                DMUON_READ(0, stage(kt + 1), 0);
+                DMUON_MFMA((KS - 1) & 1);
+                DMUON_INTERLEAVE(0);
+            }
+            // The penultimate slab: its stage, once free, takes the next tile's
+            // slab 0 whole (this tile's slab 0 again, if there is no next tile:
+            // harmless loads into a stage nothing reads any more), in flight
+            // through the last slab and the epilogue.
+            DMUON_KSTEPS(L, (KT - 1) * kBK, stage(KT - 2), stage(KT - 1));
+            wait_vm<0>();
+            if (tid == 0) s_next = wgs_x + (int)taken;
+            __syncthreads();
+            const int kn = __builtin_amdgcn_readfirstlane(s_next);  // wave-uniform
+            const bool has_next = kn < count_x;
+            TileInfo nxt = cur;
+            if (has_next) decode(kn, nxt);
+            plan_loads(nxt, L);  // this tile's plan is not needed any more
+            __builtin_amdgcn_sched_barrier(0);
+            dma_part(L, 0, stage(KT - 2), 0, C::kDmaPerOp);
+            __builtin_amdgcn_sched_barrier(0);
+            DMUON_READ(0, stage(KT - 1), 0);
+            DMUON_MFMA((KS - 1) & 1);
+            DMUON_INTERLEAVE(0);
+            // the last slab
+            _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {
+                DMUON_READ((ks + 1) & 1, stage(KT - 1), ks + 1);
+                DMUON_MFMA(ks & 1);
+                DMUON_INTERLEAVE(0);
+            }
+            DMUON_MFMA((KS - 1) & 1);
+            __syncthreads();  // every wave is done with the last slab's stage
+            epilogue(cur, stage(KT - 1));
+            if (!has_next) break;
+            // The next tile: its slab 0 sits in stage (KT - 2 + par) & 1, complete
+            // (every wave waited for its share before the epilogue's first stores,
+            // and the epilogue's barriers published it); slab 1's first piece goes
+            // into the stage the epilogue has finished with.  The epilogue's
+            // stores drain while the next tile runs.
+            __syncthreads();
+            par = (KT + par) & 1;
+            cur = nxt;
+            dma_part(L, kBK, stage(1), 0, kPiece1);
+        }
     }
+#undef DMUON_KSTEPS
+#undef DMUON_INTERLEAVE
+#undef DMUON_READ
+#undef DMUON_READ_A
+#undef DMUON_MFMA
+    // no load into LDS may outlive the workgroup; then the last workgroup of
+    // the launch empties the queues for the next launch
+    wait_vm<0>();
+    if (tid == 0) {
+        __threadfence();
+        const uint32_t done = atomicAdd(args.queue + kXcds, 1u);
+        if (done == gridDim.x - 1) {
+            for (int i = 0; i <= kXcds; ++i) args.queue[i] = 0u;
+        }
+    }
+}
+
+// Workgroups per XCD of a persistent launch: one per CU for 256-tiles (their
+// two 64 KB stages fill a CU's LDS), two per CU for 128-tiles; never more than
+// the XCD has tiles.
+template <int T>
+int persistent_grid(int tiles) {
+    constexpr int kCusPerXcd = 32, kPerCu = T == 256 ? 1 : 2;
+    const int per_xcd = (tiles + kXcds - 1) / kXcds;
+    return kXcds * (per_xcd < kCusPerXcd * kPerCu ? per_xcd : kCusPerXcd * kPerCu);
 }
 
 template <int T>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.total_blocks), block(TileCfg<T>::NT);
+    const dim3 grid((unsigned)persistent_grid<T>(a.total_blocks)), block(TileCfg<T>::NT);
     switch (a.phase) {
         case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram>), grid, block, 0, stream, a); break;
         case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare>), grid, block, 0, stream, a); break;

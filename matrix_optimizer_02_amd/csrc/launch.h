@@ -15,6 +15,7 @@ constexpr int kRecChunk = 24;  // records carried by one table-writing launch
 
 struct RecChunk {
     DevMatRec* table;
+    uint32_t* queue;  // the tile-queue counters, zeroed by the launch carrying record 0
     int32_t first;
     int32_t n;
     DevMatRec rec[kRecChunk];
@@ -82,6 +83,8 @@ struct GemmSeg {
 
 struct GemmArgs {
     char* ws;
+    uint32_t* queue;     // bf16: kQueueWords counters, zero at launch (kXcds tile counters, then the
+                         // count of finished workgroups); the launch's last workgroup zeroes them again
     const float* scale;  // per plan index: 1 / (||U|| + eps)
     float a, b, c;
     int32_t phase;

@@ -213,6 +213,8 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
         off = align_up(off + sizeof(float) * (std::size_t)count);
         p->off_partials = off;
         off = align_up(off + sizeof(float) * (std::size_t)partials);
+        p->off_queue = off;
+        off = align_up(off + sizeof(uint32_t) * (std::size_t)kQueueWords);
         for (BucketPlan& bp : p->buckets) {
             const std::size_t cnt = bp.members.size();
             const std::size_t xsz = (std::size_t)bp.m_pad * bp.n_pad * bp.esize;
