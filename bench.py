@@ -34,8 +34,14 @@ context.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of
 the same workload (one matrix per distinct shape and orientation) and
 extrapolates it to the whole set by multiplicity, with single-thread oracle
 times of the two small workloads.  ``small_workloads`` gives those two
-workloads' graph-replayed step times on the GPU.  ``clock`` samples the shader
-clock and the socket power through amdsmi during the timed steps.
+workloads' graph-replayed step times on the GPU.  ``power`` samples the socket
+power through amdsmi during the timed steps; ``clock`` is the shader clock read
+by the library's sampler kernel over as many steps again, in a pass of its own.
+``ceilings`` measures, in the same run, what the chip sustains outside this
+library: a streaming copy (the practical HBM ceiling) and a matrix-core burn
+on pseudo-random bf16 operands with no memory traffic (the bf16 rate the
+power limit allows); the roofline and the elementwise passes are also given
+as fractions of these.
 """
 
 from __future__ import annotations
@@ -52,7 +58,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector/matrix
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix (v_mfma_f32_*_f32)
 HBM_PEAK_BPS = 8.0e12       # MI355X HBM3E
 NS_STEPS = 5
 LR, BETA, EPS = 0.02, 0.95, 1e-7
@@ -105,7 +111,7 @@ def dominant_kernel(seg_len, resident, bx_flops_grouped, res_flops, bx_ms_per_st
     if grouped_len:
         bx_iters = [k for k in range(steps) if any(k % L == L - 1 or k == steps - 1 for L in grouped_len)]
         bx_ms = [row[k] for row in bx_ms_per_step for k in bx_iters]
-        kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X))" if f32_only
+        kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X), fp32 MFMA)" if f32_only
                   else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)")
         return kernel, sum(bx_ms) / len(bx_ms), bx_flops_grouped / len(bx_iters)
     return ("ns_resident_kernel (every iteration of a small bf16 bucket in one launch, the matrix in LDS)",
@@ -184,6 +190,67 @@ def cpu_baseline(w, host_samples, gpu_ms_per_step):
     return out
 
 
+def ceilings(d, dev, copy_bytes: int = 1 << 30, mfma_seconds: float = 0.5):
+    """What the chip sustains outside the library, measured in this run: a
+    streaming copy of copy_bytes (read + write bytes per second) and a
+    matrix-core burn on pseudo-random bf16 operands for about mfma_seconds
+    (after a warm-up of a fifth of that), with the clock read in a pass of its own."""
+    import torch
+
+    src = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        d.diag_copy(dst, src)
+    e0.record()
+    reps = 5
+    for _ in range(reps):
+        d.diag_copy(dst, src)
+    e1.record()
+    e1.synchronize()
+    copy_bps = 2 * copy_bytes * reps / (e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    iters = 4096
+    flops = d.diag_mfma(out, blocks, iters)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    d.diag_mfma(out, blocks, iters)
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-4)
+    n = max(10, int(mfma_seconds / per))
+    for _ in range(max(2, n // 5)):
+        d.diag_mfma(out, blocks, iters)
+    power = PowerSampler()
+    power.start()
+    e0.record()
+    for _ in range(n):
+        d.diag_mfma(out, blocks, iters)
+    e1.record()
+    e1.synchronize()
+    power.stop()
+    seconds = e0.elapsed_time(e1) / 1e3
+    mfma_tflops = flops * n / seconds / 1e12
+    m = max(4, n // 2)
+
+    def burn():
+        for _ in range(m):
+            d.diag_mfma(out, blocks, iters)
+
+    clock = sample_clock(d, dev, burn, seconds * m / n)
+    power_summary = power.summary()
+    power.close()
+    return {"copy": {"bytes_per_pass": 2 * copy_bytes, "tbps": round(copy_bps / 1e12, 3),
+                     "frac_hbm_peak": round(copy_bps / HBM_PEAK_BPS, 4),
+                     "kernel": "dmuon_diag_copy: streaming 16-byte loads and stores, four per lane in flight"},
+            "mfma_bf16": {"tflops": round(mfma_tflops, 1), "frac_bf16_peak": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+                          "launches": n, "seconds": round(seconds, 3),
+                          "kernel": "dmuon_diag_mfma: v_mfma_f32_32x32x16_bf16 back to back on pseudo-random "
+                                    "operands, no memory traffic",
+                          "power": power_summary, "clock": clock}}
+
+
 def small_workloads(d, dev, reps: int = 200, oracle_single_thread: bool = True):
     """The two small workloads (the fp32 256 x 512 matrix and the 96-matrix bf16
     batch): graph-replayed GPU step time and matrices/s, and the oracle's time
@@ -222,11 +289,11 @@ def small_workloads(d, dev, reps: int = 200, oracle_single_thread: bool = True):
     return out
 
 
-class ClockSampler:
-    """Samples the shader clock and the socket power through amdsmi (the GPU
-    metrics table the driver refreshes) on a host thread, every ``period``
-    seconds between start() and stop().  Records nothing but an error string
-    where amdsmi is unavailable."""
+class PowerSampler:
+    """Samples the socket power through amdsmi (the GPU metrics table the
+    driver refreshes) on a host thread, every ``period`` seconds between
+    start() and stop().  Records nothing but an error string where amdsmi is
+    unavailable."""
 
     def __init__(self, period: float = 0.005):
         self.period = period
@@ -245,16 +312,15 @@ class ClockSampler:
         except Exception as e:  # pragma: no cover - depends on the box
             self.error = f"{type(e).__name__}: {e}"
 
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        return {"t": time.perf_counter(), "gfxclk": clks, "avg_gfxclk": m.get("average_gfxclk_frequency"),
-                "power": m.get("current_socket_power"), "avg_power": m.get("average_socket_power")}
+    @staticmethod
+    def _num(v):
+        return isinstance(v, (int, float)) and 0 < v < 10000
 
     def _loop(self):
         while not self._stop.is_set():
             try:
-                self.samples.append(self._read())
+                m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+                self.samples.append(m.get("current_socket_power"))
             except Exception as e:  # pragma: no cover
                 self.error = f"{type(e).__name__}: {e}"
                 return
@@ -275,22 +341,53 @@ class ClockSampler:
             self._thread.join()
 
     def summary(self):
-        if self._h is None or not self.samples:
-            return {"source": "amdsmi gpu metrics", "error": self.error or "no samples"}
-        clk = [sum(s["gfxclk"]) / len(s["gfxclk"]) for s in self.samples if s["gfxclk"]]
-        pw = [s["power"] for s in self.samples if isinstance(s["power"], (int, float)) and 0 < s["power"] < 10000]
-        stat = lambda v: ({"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v)} if v else None)
-        try:
-            self._amdsmi.amdsmi_shut_down()
-        except Exception:  # pragma: no cover
-            pass
-        return {"source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, current_socket_power), "
-                          f"sampled every {self.period * 1e3:.0f} ms during the timed steps",
-                "samples": len(self.samples), "sclk_mhz": stat(clk), "socket_power_w": stat(pw),
-                "perf_level": getattr(self, "perf_level", None),
-                "bf16_peak_at_mean_sclk_tflops": (round(BF16_PEAK_TFLOPS * (sum(clk) / len(clk)) / 2400.0, 1)
-                                                  if clk else None),
-                "error": self.error}
+        pw = [v for v in self.samples if self._num(v)]
+        out = {"source": f"amdsmi current_socket_power, sampled every {self.period * 1e3:.0f} ms",
+               "perf_level": getattr(self, "perf_level", None), "samples": len(pw)}
+        if pw:
+            out.update({"mean_w": round(sum(pw) / len(pw), 1), "min_w": min(pw), "max_w": max(pw)})
+        if self.error:
+            out["error"] = self.error
+        return out
+
+    def close(self):
+        if self._h is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # pragma: no cover
+                pass
+            self._h = None
+
+
+def sample_clock(d, dev, enqueue, expected_s: float):
+    """The shader clock while ``enqueue()``'s work runs: the library's clock
+    sampler (one wave reading the shader-clock counter against the 100 MHz wall
+    clock) on a side stream of default priority, started just before the work
+    and sized to end within it (90% of expected_s).  The wave takes a slot on
+    one CU, which can hold back one workgroup of a full-chip launch, so this is
+    a pass of its own beside the timed one; its own duration is returned too."""
+    import torch
+
+    span = max(0.9 * expected_s, 2e-3)
+    samples = min(4096, max(2, int(span / 1e-3) + 1))
+    interval = max(1, int(span * 1e8 / (samples - 1)))
+    buf = torch.zeros(2 * samples, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    d.diag_clock(buf, samples, interval, stream=side)
+    t0 = time.perf_counter()
+    enqueue()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    v = buf.view(samples, 2).cpu().tolist()
+    rates = [(c1 - c0) / (w1 - w0) * 100.0 for (c0, w0), (c1, w1) in zip(v, v[1:]) if w1 > w0]
+    mean = (v[-1][0] - v[0][0]) / max(v[-1][1] - v[0][1], 1) * 100.0
+    return {"source": "dmuon_diag_clock: shader-clock counter against the 100 MHz wall clock, one wave on a side "
+                      "stream (the clock of the XCD it ran on)",
+            "mean_mhz": round(mean, 1), "min_mhz": round(min(rates), 1) if rates else None,
+            "max_mhz": round(max(rates), 1) if rates else None, "samples": samples,
+            "interval_ms": round(interval / 1e5, 3), "pass_seconds": round(wall, 4),
+            "bf16_peak_at_mean_mhz_tflops": round(BF16_PEAK_TFLOPS * mean / 2400.0, 1)}
 
 
 def graph_bench(d, plan, G, M, W, ws, reps: int, count: int):
@@ -394,6 +491,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-small-workloads", action="store_true",
                     help="skip the two small workloads' graph-replayed step times")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the copy and matrix-core ceilings")
     ap.add_argument("--tuning-cache", default=None, metavar="PATH",
                     help="run the plan with per-shape tuning entries: loaded from PATH for this device, "
                          "or measured with muon_autotune on the benchmark inputs and saved there")
@@ -467,16 +566,16 @@ def main(argv=None):
     for _ in range(args.warmup):
         d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
     events = [d.PhaseEvents(NS_STEPS) for _ in range(args.steps)]
-    clock = ClockSampler()
+    power = PowerSampler()
     torch.cuda.synchronize()
-    clock.start()
+    power.start()
     t0 = time.perf_counter()
     for k in range(args.steps):
         d.muon_step_batched_profiled(plan, G, M, W, events[k], lr=LR, beta=BETA, eps=EPS,
                                      workspace=ws, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    clock.stop()
+    power.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     names = events[0].names()
@@ -552,7 +651,7 @@ def main(argv=None):
         "matrices_per_s": round(w.count / step_s, 2),
         "phase_ms": {k: round(v, 4) for k, v in avg.items()},
         "gemm_ms_per_step": round(sum(gemm_ms) / len(per), 4),
-        "roofline": {"bound": "alu" if f32_only else "mfma", "kernel": kernel,
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "launch_ms": round(launch_ms, 4), "flops_per_launch": flops_per_launch},
@@ -580,7 +679,24 @@ def main(argv=None):
         out["torch_baseline"] = tb
     if not args.no_adamw:
         out["adamw"] = adamw_bench(d, dev)
-    out["clock"] = clock.summary()
+    out["power"] = power.summary()
+    power.close()
+
+    def clocked_steps():
+        for _ in range(args.steps):
+            d.muon_step_batched(plan, G, M, W, lr=LR, beta=BETA, eps=EPS, ns_steps=NS_STEPS, workspace=ws)
+
+    out["clock"] = sample_clock(d, dev, clocked_steps, ms_per_step * args.steps / 1e3)
+    out["clock"]["pass"] = f"{args.steps} more steps after the timed ones, with the sampler beside them"
+    if not args.no_ceilings:
+        ce = ceilings(d, dev)
+        out["ceilings"] = ce
+        out["roofline"]["frac_of_sustained_mfma"] = (round(achieved / ce["mfma_bf16"]["tflops"], 4)
+                                                     if not f32_only else None)
+        for k in ("prep", "apply"):
+            out["elementwise"][k]["frac_of_copy"] = round(out["elementwise"][k]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
+        if "adamw" in out:
+            out["adamw"]["frac_of_copy"] = round(out["adamw"]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
     if not args.no_small_workloads and args.workload not in ("f32_256x512", "bf16_small_batch_96"):
         out["small_workloads"] = small_workloads(d, dev, oracle_single_thread=not args.no_cpu_baseline)
     if host_samples:

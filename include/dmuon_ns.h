@@ -400,6 +400,36 @@ DMUON_API dmuon_status dmuon_events_elapsed_ms(void* start, void* stop, float* m
 /* Destroy n events created by dmuon_events_create (NULL entries skipped). */
 DMUON_API dmuon_status dmuon_events_destroy(int32_t n, void** events);
 
+/* ---- measurement ------------------------------------------------------------
+ * Two kernels that measure the practical ceilings the benchmark reports next
+ * to the published peaks, on the same device in the same run (the project's
+ * benchmark section states hardware, precision and method for every figure:
+ * DMuon project documentation, "基准测试").  Both only enqueue on `stream`.
+ *
+ * dmuon_diag_copy: copy `bytes` (a multiple of 16, > 0) from src to dst
+ * (device, 16-byte aligned, not overlapping) with streaming 16-byte accesses:
+ * the HBM read + write rate a bandwidth-bound pass can reach.  INVALID_ARG for
+ * bad pointers or sizes, HIP on a launch failure. */
+DMUON_API dmuon_status dmuon_diag_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* dmuon_diag_mfma: `blocks` workgroups of 512 threads, each wave running
+ * `iters` (a multiple of 8) rounds of 8 independent v_mfma_f32_32x32x16_bf16
+ * (32768 flops each) on pseudo-random bf16 operands that change every
+ * instruction, with no memory traffic: 8 * blocks * iters * 8 * 32768 flops,
+ * the matrix-core rate the chip sustains within its power limit.  out: device,
+ * blocks * 512 floats (per-thread sums that keep the products live).
+ * INVALID_ARG for bad arguments, HIP on a launch failure. */
+DMUON_API dmuon_status dmuon_diag_mfma(float* out, int32_t blocks, int32_t iters, void* stream);
+
+/* dmuon_diag_clock: one wave that records `samples` (>= 2) pairs (shader-clock
+ * cycles, 100 MHz wall-clock ticks) into out (device, 2 * samples int64), the
+ * k-th pair k * interval wall ticks (>= 1) after the first; it runs for
+ * samples x interval ticks, at most 1e10 (100 s).  Launched on a stream of its
+ * own beside other work, the pairs give the shader clock of the XCD it ran on
+ * while that work ran.  INVALID_ARG for bad arguments, HIP on a launch
+ * failure. */
+DMUON_API dmuon_status dmuon_diag_clock(long long* out, int32_t samples, int32_t interval, void* stream);
+
 /* Static, human-readable name of a status code. */
 DMUON_API const char* dmuon_status_string(dmuon_status status);
 

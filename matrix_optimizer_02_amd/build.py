@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdmuon_ns.so")
 
-HIP_SOURCES = ["api.hip", "k_adamw.hip", "k_elementwise.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip", "k_resident.hip",
-               "tune.hip"]
+HIP_SOURCES = ["api.hip", "k_adamw.hip", "k_diag.hip", "k_elementwise.hip", "k_gemm_bf16.hip", "k_gemm_f32.hip",
+               "k_resident.hip", "tune.hip"]
 CXX_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

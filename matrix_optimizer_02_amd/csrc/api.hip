@@ -139,15 +139,17 @@ hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const Step
         for (const SegSpec& ss : segs) {
             const BucketPlan& bp = *ss.bp;
             if (bp.path != tc.path || bp.tile != tc.tile) continue;
-            const int64_t tm = bp.m_pad / bp.tile, tn = bp.n_pad / bp.tile;
+            // the kernel's output tile: the bucket's on the bf16 path, the fp32 kernels' own on fp32
+            const int64_t ktile = bp.path == kPathF32 ? f32_kernel_tile() : bp.tile;
+            const int64_t tm = bp.m_pad / ktile, tn = bp.n_pad / ktile;
             const int64_t blocks = (int64_t)bp.members.size() * (phase == kBX ? tm * tn : tm * (tm + 1) / 2);
             if (ga.nseg == kMaxSeg || (int64_t)ga.total_blocks + blocks > (int64_t)INT32_MAX) {
                 hipError_t e = flush();
                 if (e != hipSuccess) return e;
             }
             GemmSeg& s = ga.seg[ga.nseg++];
-            s.tm = (int32_t)(bp.m_pad / bp.tile);
-            s.tn = (int32_t)(bp.n_pad / bp.tile);
+            s.tm = (int32_t)tm;
+            s.tn = (int32_t)tn;
             s.tiles_per_mat = phase == kBX ? s.tm * s.tn : s.tm * (s.tm + 1) / 2;
             s.count = (int32_t)bp.members.size();
             s.plan_base = bp.plan_base;

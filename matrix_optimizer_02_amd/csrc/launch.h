@@ -95,6 +95,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm_bf16(int tile, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);
+// Output tile edge of the fp32 kernels (their buckets are padded to 64, a multiple of it).
+int f32_kernel_tile();
 
 // ---- AdamW for the non-Muon parameters (k_adamw.hip) ------------------------
 

@@ -134,6 +134,9 @@ def _load():
         "dmuon_events_destroy": (ctypes.c_int, [ctypes.c_int32, vpp]),
         "adamw_step_batched": (ctypes.c_int, [ctypes.c_int32, c_int64_p, c_int32_p, c_int32_p, vpp, vpp, vpp,
                                               vpp, ctypes.POINTER(AdamWHParams), ctypes.c_void_p]),
+        "dmuon_diag_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "dmuon_diag_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+        "dmuon_diag_clock": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
         "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dmuon_version": (ctypes.c_char_p, []),
     }
@@ -515,6 +518,34 @@ def adamw_step_batched(params: Sequence[torch.Tensor], grads: Sequence[torch.Ten
     arrs = [ctypes.cast(_ptr_array(x), vp) for x in (params, grads, exp_avgs, exp_avg_sqs)]
     st = _lib.adamw_step_batched(n, numels, pdt, gdt, *arrs, ctypes.byref(hp), _stream_handle(stream))
     _check(st, "adamw_step_batched")
+
+
+def diag_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Enqueue the streaming copy of src into dst (same byte size, a multiple of 16)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("dst and src must have the same byte size")
+    _check(_lib.dmuon_diag_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), n,
+                                _stream_handle(stream)), "dmuon_diag_copy")
+
+
+def diag_mfma(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """Enqueue the matrix-core burn; returns the flops it performs.  out: fp32,
+    at least blocks * 512 elements."""
+    if out.dtype != torch.float32 or out.numel() < blocks * 512:
+        raise ValueError("out must be fp32 with blocks * 512 elements")
+    _check(_lib.dmuon_diag_mfma(ctypes.c_void_p(out.data_ptr()), int(blocks), int(iters), _stream_handle(stream)),
+           "dmuon_diag_mfma")
+    return 8 * blocks * iters * 8 * 32768
+
+
+def diag_clock(out: torch.Tensor, samples: int, interval_ticks: int, stream=None) -> None:
+    """Enqueue the clock sampler: out int64 with 2 * samples elements, one
+    (shader cycles, 100 MHz wall ticks) pair every interval_ticks."""
+    if out.dtype != torch.int64 or not out.is_cuda or out.numel() < 2 * samples:
+        raise ValueError("out must be a device int64 tensor with 2 * samples elements")
+    _check(_lib.dmuon_diag_clock(ctypes.c_void_p(out.data_ptr()), int(samples), int(interval_ticks),
+                                 _stream_handle(stream)), "dmuon_diag_clock")
 
 
 class PhaseEvents:

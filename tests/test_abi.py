@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol():
                           "muon_step_batched", "muon_step_batched_noalloc",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
-                          "adamw_step_batched", "dmuon_status_string", "dmuon_version"}
+                          "adamw_step_batched", "dmuon_status_string", "dmuon_version",
+                          "dmuon_diag_copy", "dmuon_diag_mfma", "dmuon_diag_clock"}
     for n in names:
         assert hasattr(raw, n), n
 
