@@ -263,9 +263,9 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         r.x_off1 = (int64_t)bp.off_x1 + mp.slot * xsz;
         r.partial_off = mp.partial_off;
         r.prep_begin = prep_blocks;
-        prep_blocks += mp.prep_tiles;
+        prep_blocks += prep_blocks_of(mp.r_pad, mp.c_pad);
         r.apply_begin = apply_blocks;
-        apply_blocks += ((mp.rows + kPrepTile - 1) / kPrepTile) * ((mp.cols + kPrepTile - 1) / kPrepTile);
+        apply_blocks += apply_blocks_of(mp.rows, mp.cols);
         r.rows = (int32_t)mp.rows;
         r.cols = (int32_t)mp.cols;
         r.r_pad = (int32_t)mp.r_pad;

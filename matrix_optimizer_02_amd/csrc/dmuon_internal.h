@@ -14,8 +14,21 @@ constexpr int kPathF32 = DMUON_F32;
 constexpr int kPathBF16 = DMUON_BF16;
 
 // Elementwise kernels work on 64 x 64 tiles of the padded stored-orientation
-// matrix; every tile granularity is a multiple of 64.
+// matrix; every tile granularity is a multiple of 64.  A prep or apply block
+// takes kTilesPerBlock neighbouring tiles along the stored row (the last block
+// of a row fewer when the row has an odd number of tiles): twice the bytes in
+// flight per block, measured 3-4% faster than one tile on the 8B-model shapes.
 constexpr int kPrepTile = 64;
+constexpr int kTilesPerBlock = 2;
+// Blocks of a prep pass over an r_pad x c_pad grid and of an apply pass over
+// a rows x cols matrix.
+inline int64_t prep_blocks_of(int64_t r_pad, int64_t c_pad) {
+    return (r_pad / kPrepTile) * ((c_pad / kPrepTile + kTilesPerBlock - 1) / kTilesPerBlock);
+}
+inline int64_t apply_blocks_of(int64_t rows, int64_t cols) {
+    const int64_t tc = (cols + kPrepTile - 1) / kPrepTile;
+    return ((rows + kPrepTile - 1) / kPrepTile) * ((tc + kTilesPerBlock - 1) / kTilesPerBlock);
+}
 constexpr std::size_t kAlign = 256;
 // Gram-space iterations between restarts unless the plan options say
 // otherwise: 2 on buckets of padded short side up to 1024, 3 above.  Measured
