@@ -38,10 +38,11 @@ workloads' graph-replayed step times on the GPU.  ``power`` samples the socket
 power through amdsmi during the timed steps; ``clock`` is the shader clock read
 by the library's sampler kernel over as many steps again, in a pass of its own.
 ``ceilings`` measures, in the same run, what the chip sustains outside this
-library: a streaming copy (the practical HBM ceiling) and a matrix-core burn
-on pseudo-random bf16 operands with no memory traffic (the bf16 rate the
-power limit allows); the roofline and the elementwise passes are also given
-as fractions of these.
+library: a streaming copy (the practical HBM ceiling), each bandwidth-bound
+pass's own byte mix (dtypes, streams, read/write ratio) on flat contiguous
+arrays, and a matrix-core burn on pseudo-random bf16 operands with no memory
+traffic (the bf16 rate the power limit allows); the roofline and the
+elementwise passes are also given as fractions of these.
 """
 
 from __future__ import annotations
@@ -210,6 +211,25 @@ def ceilings(d, dev, copy_bytes: int = 1 << 30, mfma_seconds: float = 0.5):
     e1.synchronize()
     copy_bps = 2 * copy_bytes * reps / (e0.elapsed_time(e1) / 1e3)
     del src, dst
+    # each bandwidth-bound pass's own byte mix, flat and contiguous, far beyond the 256 MB last-level cache
+    mix = {}
+    n_mix = 1 << 28
+    for kind in ("prep", "apply", "adamw"):
+        a = torch.zeros(n_mix, dtype=torch.bfloat16, device=dev)
+        b = torch.zeros(n_mix, dtype=torch.float32 if kind == "prep" else torch.bfloat16, device=dev)
+        c = (torch.zeros(n_mix, dtype=torch.bfloat16, device=dev) if kind == "prep" else
+             torch.zeros(2 * n_mix, dtype=torch.float32, device=dev) if kind == "adamw" else None)
+        for _ in range(2):
+            nbytes = d.diag_mix(kind, a, b, c)
+        e0.record()
+        for _ in range(reps):
+            d.diag_mix(kind, a, b, c)
+        e1.record()
+        e1.synchronize()
+        bps = nbytes * reps / (e0.elapsed_time(e1) / 1e3)
+        mix[kind] = {"elements": n_mix, "bytes_per_pass": nbytes, "tbps": round(bps / 1e12, 3),
+                     "frac_hbm_peak": round(bps / HBM_PEAK_BPS, 4)}
+        del a, b, c
     blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
     iters = 4096
@@ -244,6 +264,8 @@ def ceilings(d, dev, copy_bytes: int = 1 << 30, mfma_seconds: float = 0.5):
     return {"copy": {"bytes_per_pass": 2 * copy_bytes, "tbps": round(copy_bps / 1e12, 3),
                      "frac_hbm_peak": round(copy_bps / HBM_PEAK_BPS, 4),
                      "kernel": "dmuon_diag_copy: streaming 16-byte loads and stores, four per lane in flight"},
+            "mix": dict(mix, kernel="dmuon_diag_mix: each pass's dtypes, streams and read/write bytes on flat "
+                                    "contiguous arrays, four 4-element groups per lane in flight"),
             "mfma_bf16": {"tflops": round(mfma_tflops, 1), "frac_bf16_peak": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
                           "launches": n, "seconds": round(seconds, 3),
                           "kernel": "dmuon_diag_mfma: v_mfma_f32_32x32x16_bf16 back to back on pseudo-random "
@@ -695,8 +717,10 @@ def main(argv=None):
                                                      if not f32_only else None)
         for k in ("prep", "apply"):
             out["elementwise"][k]["frac_of_copy"] = round(out["elementwise"][k]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
+            out["elementwise"][k]["frac_of_mix"] = round(out["elementwise"][k]["gbps"] / (ce["mix"][k]["tbps"] * 1e3), 4)
         if "adamw" in out:
             out["adamw"]["frac_of_copy"] = round(out["adamw"]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
+            out["adamw"]["frac_of_mix"] = round(out["adamw"]["gbps"] / (ce["mix"]["adamw"]["tbps"] * 1e3), 4)
     if not args.no_small_workloads and args.workload not in ("f32_256x512", "bf16_small_batch_96"):
         out["small_workloads"] = small_workloads(d, dev, oracle_single_thread=not args.no_cpu_baseline)
     if host_samples:

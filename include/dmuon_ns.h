@@ -421,6 +421,17 @@ DMUON_API dmuon_status dmuon_diag_copy(void* dst, const void* src, size_t bytes,
  * INVALID_ARG for bad arguments, HIP on a launch failure. */
 DMUON_API dmuon_status dmuon_diag_mfma(float* out, int32_t blocks, int32_t iters, void* stream);
 
+/* dmuon_diag_mix: the byte mix of one of the library's bandwidth-bound
+ * passes on flat contiguous arrays of n elements (n > 0, a multiple of 4), so
+ * that a pass can be compared with what its own traffic reaches untiled.
+ * kind 0 (prep): reads a (bf16, n) and b (fp32, n), writes b and c (bf16, n):
+ * 12 bytes an element.  kind 1 (apply): reads a and b (bf16, n), writes b; c
+ * unused: 6 bytes.  kind 2 (AdamW): reads a and b (bf16, n) and c (fp32,
+ * 2 n), writes a and c: 22 bytes.  Device pointers, 16-byte aligned, regions
+ * not overlapping; the arrays' contents are overwritten with bounded values.
+ * INVALID_ARG for bad arguments, HIP on a launch failure. */
+DMUON_API dmuon_status dmuon_diag_mix(int32_t kind, void* a, void* b, void* c, size_t n, void* stream);
+
 /* dmuon_diag_clock: one wave that records `samples` (>= 2) pairs (shader-clock
  * cycles, 100 MHz wall-clock ticks) into out (device, 2 * samples int64), the
  * k-th pair k * interval wall ticks (>= 1) after the first; it runs for

@@ -2,6 +2,9 @@
 // to the published peaks, measured on the same device in the same run.
 //   copy  -- a streaming copy (non-temporal 16-byte accesses, four per lane in
 //            flight): the HBM read + write rate a bandwidth-bound pass can reach;
+//   mix   -- the byte mix of one of the library's bandwidth-bound passes (the
+//            same dtypes, streams and read/write ratio) on flat contiguous
+//            arrays: what that pass's traffic can reach without its tiling;
 //   mfma  -- back-to-back v_mfma_f32_32x32x16_bf16 on operands that change every
 //            instruction (pseudo-random bf16 values, as the products of the
 //            Newton-Schulz iteration see), no memory traffic: the matrix-core
@@ -35,6 +38,65 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(f32x4_t* __restrict_
         for (int u = 0; u < kCopyVec; ++u) {
             const int64_t i = base + (int64_t)u * kCopyThreads;
             if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+        }
+    }
+}
+
+// kind 0, prep: read a (bf16) and b (fp32), write b and c (bf16), 12 bytes an
+// element; kind 1, apply: read a and b (bf16), write b, 6 bytes; kind 2,
+// AdamW: read a and b (bf16) and c, c + n (fp32), write a, c and c + n, 22
+// bytes.  Four elements a group, four groups per lane in flight, grid-stride.
+template <int KIND>
+__global__ __launch_bounds__(kCopyThreads) void mix_kernel(void* a, void* b, void* c, int64_t n4) {
+    const int64_t n = 4 * n4;
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads * kCopyVec;
+    for (int64_t base = ((int64_t)blockIdx.x * kCopyThreads * kCopyVec) + threadIdx.x; base < n4; base += stride) {
+        float4 x[kCopyVec], y[kCopyVec], z[kCopyVec], w[kCopyVec];
+        #pragma unroll
+        for (int u = 0; u < kCopyVec; ++u) {
+            const int64_t e = 4 * (base + (int64_t)u * kCopyThreads);
+            if (e >= n) continue;
+            if (KIND == 0) {
+                x[u] = load4(static_cast<const uint16_t*>(a) + e);
+                y[u] = load4(static_cast<const float*>(b) + e);
+            } else if (KIND == 1) {
+                x[u] = load4(static_cast<const uint16_t*>(a) + e);
+                y[u] = load4(static_cast<const uint16_t*>(b) + e);
+            } else {
+                x[u] = load4(static_cast<const uint16_t*>(a) + e);
+                y[u] = load4(static_cast<const uint16_t*>(b) + e);
+                z[u] = load4(static_cast<const float*>(c) + e);
+                w[u] = load4(static_cast<const float*>(c) + n + e);
+            }
+        }
+        #pragma unroll
+        for (int u = 0; u < kCopyVec; ++u) {
+            const int64_t e = 4 * (base + (int64_t)u * kCopyThreads);
+            if (e >= n) continue;
+            if (KIND == 0) {
+                const float4 m = make_float4(fmaf(0.95f, y[u].x, x[u].x), fmaf(0.95f, y[u].y, x[u].y),
+                                             fmaf(0.95f, y[u].z, x[u].z), fmaf(0.95f, y[u].w, x[u].w));
+                store4(static_cast<float*>(b) + e, m);
+                store4(static_cast<uint16_t*>(c) + e,
+                       make_float4(fmaf(0.95f, m.x, x[u].x), fmaf(0.95f, m.y, x[u].y), fmaf(0.95f, m.z, x[u].z),
+                                   fmaf(0.95f, m.w, x[u].w)));
+            } else if (KIND == 1) {
+                store4(static_cast<uint16_t*>(b) + e,
+                       make_float4(fmaf(-1e-3f, x[u].x, y[u].x), fmaf(-1e-3f, x[u].y, y[u].y),
+                                   fmaf(-1e-3f, x[u].z, y[u].z), fmaf(-1e-3f, x[u].w, y[u].w)));
+            } else {
+                float p[4] = {x[u].x, x[u].y, x[u].z, x[u].w}, g[4] = {y[u].x, y[u].y, y[u].z, y[u].w};
+                float m[4] = {z[u].x, z[u].y, z[u].z, z[u].w}, v[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    m[q] = fmaf(0.9f, m[q], 0.1f * g[q]);
+                    v[q] = fmaf(0.999f, v[q], 1e-3f * g[q] * g[q]);
+                    p[q] = fmaf(-1e-4f, m[q] / (sqrtf(v[q]) + 1e-8f), p[q]);
+                }
+                store4(static_cast<uint16_t*>(a) + e, make_float4(p[0], p[1], p[2], p[3]));
+                store4(static_cast<float*>(c) + e, make_float4(m[0], m[1], m[2], m[3]));
+                store4(static_cast<float*>(c) + n + e, make_float4(v[0], v[1], v[2], v[3]));
+            }
         }
     }
 }
@@ -130,6 +192,31 @@ extern "C" dmuon_status dmuon_diag_copy(void* dst, const void* src, size_t bytes
     if (blocks > 256 * 64) blocks = 256 * 64;  // a grid-stride loop covers the rest
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<f32x4_t*>(dst), static_cast<const f32x4_t*>(src), n16);
+    return hipGetLastError() == hipSuccess ? DMUON_OK : DMUON_ERR_HIP;
+}
+
+extern "C" dmuon_status dmuon_diag_mix(int32_t kind, void* a, void* b, void* c, size_t n, void* stream) {
+    if (kind < 0 || kind > 2 || n == 0 || n % 4 != 0 || n > ((size_t)1 << 40)) return DMUON_ERR_INVALID_ARG;
+    const size_t a_bytes = 2 * n, b_bytes = kind == 0 ? 4 * n : 2 * n, c_bytes = kind == 0 ? 2 * n : 8 * n;
+    void* ptrs[3] = {a, b, c};
+    const size_t sizes[3] = {a_bytes, b_bytes, kind == 1 ? 0 : c_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (sizes[i] == 0) continue;
+        if (ptrs[i] == nullptr || (reinterpret_cast<uintptr_t>(ptrs[i]) & 15u) != 0) return DMUON_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j) {
+            if (sizes[j] == 0) continue;
+            const uintptr_t x = reinterpret_cast<uintptr_t>(ptrs[i]), y = reinterpret_cast<uintptr_t>(ptrs[j]);
+            if (x < y + sizes[j] && y < x + sizes[i]) return DMUON_ERR_INVALID_ARG;  // overlapping
+        }
+    }
+    const int64_t n4 = (int64_t)(n / 4);
+    int64_t blocks = (n4 + kCopyThreads * kCopyVec - 1) / (kCopyThreads * kCopyVec);
+    if (blocks > 256 * 64) blocks = 256 * 64;  // a grid-stride loop covers the rest
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(kCopyThreads);
+    if (kind == 0) hipLaunchKernelGGL(mix_kernel<0>, grid, block, 0, s, a, b, c, n4);
+    else if (kind == 1) hipLaunchKernelGGL(mix_kernel<1>, grid, block, 0, s, a, b, c, n4);
+    else hipLaunchKernelGGL(mix_kernel<2>, grid, block, 0, s, a, b, c, n4);
     return hipGetLastError() == hipSuccess ? DMUON_OK : DMUON_ERR_HIP;
 }
 

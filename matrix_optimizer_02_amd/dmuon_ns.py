@@ -137,6 +137,8 @@ def _load():
         "dmuon_diag_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
         "dmuon_diag_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
         "dmuon_diag_clock": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+        "dmuon_diag_mix": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]),
         "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "dmuon_version": (ctypes.c_char_p, []),
     }
@@ -537,6 +539,29 @@ def diag_mfma(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
     _check(_lib.dmuon_diag_mfma(ctypes.c_void_p(out.data_ptr()), int(blocks), int(iters), _stream_handle(stream)),
            "dmuon_diag_mfma")
     return 8 * blocks * iters * 8 * 32768
+
+
+MIX_KINDS = {"prep": (0, 12), "apply": (1, 6), "adamw": (2, 22)}  # kind, bytes per element
+
+
+def diag_mix(kind: str, a: torch.Tensor, b: torch.Tensor, c: Optional[torch.Tensor] = None, stream=None) -> int:
+    """Enqueue the flat byte-mix kernel of one pass ('prep', 'apply' or
+    'adamw'; a: bf16 n elements, b: fp32 for prep else bf16, n elements, c:
+    bf16 n for prep, fp32 2 n for adamw, unused for apply).  Returns the bytes
+    it moves."""
+    k, per = MIX_KINDS[kind]
+    n = a.numel()
+    want_b = torch.float32 if kind == "prep" else torch.bfloat16
+    if a.dtype != torch.bfloat16 or b.dtype != want_b or b.numel() != n:
+        raise ValueError("a must be bf16 and b " + str(want_b) + " with as many elements")
+    if kind == "prep" and (c is None or c.dtype != torch.bfloat16 or c.numel() != n):
+        raise ValueError("prep: c must be bf16 with n elements")
+    if kind == "adamw" and (c is None or c.dtype != torch.float32 or c.numel() != 2 * n):
+        raise ValueError("adamw: c must be fp32 with 2 n elements")
+    cp = ctypes.c_void_p(c.data_ptr()) if (c is not None and kind != "apply") else ctypes.c_void_p(0)
+    _check(_lib.dmuon_diag_mix(k, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), cp, n,
+                               _stream_handle(stream)), "dmuon_diag_mix")
+    return per * n
 
 
 def diag_clock(out: torch.Tensor, samples: int, interval_ticks: int, stream=None) -> None:

@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
                           "dmuon_events_create", "dmuon_events_elapsed_ms", "dmuon_events_destroy",
                           "adamw_step_batched", "dmuon_status_string", "dmuon_version",
-                          "dmuon_diag_copy", "dmuon_diag_mfma", "dmuon_diag_clock"}
+                          "dmuon_diag_copy", "dmuon_diag_mfma", "dmuon_diag_clock",
+                          "dmuon_diag_mix"}
     for n in names:
         assert hasattr(raw, n), n
 

@@ -51,3 +51,36 @@ def test_clock_sampler_is_paced_by_the_wall_clock():
     assert 100.0 < mhz < 3000.0, mhz
     with pytest.raises(d.DMuonError):
         d.diag_clock(buf, 1, interval)
+
+
+@pytest.mark.parametrize("kind", ["prep", "apply", "adamw"])
+def test_mix_kernels_compute_their_update(kind):
+    n = 4 * 1000 + 1024 * 4  # not a multiple of a block's share
+    gen = torch.Generator().manual_seed(7)
+    a = torch.randn(n, generator=gen).to(torch.bfloat16).cuda()
+    b = torch.randn(n, generator=gen).to(torch.float32 if kind == "prep" else torch.bfloat16).cuda()
+    c = (torch.zeros(n, dtype=torch.bfloat16).cuda() if kind == "prep" else
+         torch.rand(2 * n, generator=gen).cuda() if kind == "adamw" else None)
+    a0, b0, c0 = a.float().cpu(), b.float().cpu(), None if c is None else c.float().cpu()
+    nbytes = d.diag_mix(kind, a, b, c)
+    torch.cuda.synchronize()
+    assert nbytes == d.MIX_KINDS[kind][1] * n
+    if kind == "prep":
+        m = 0.95 * b0 + a0
+        assert torch.allclose(b.cpu(), m, rtol=1e-6, atol=1e-6)
+        assert torch.allclose(c.float().cpu(), 0.95 * m + a0, rtol=1e-2, atol=1e-2)
+    elif kind == "apply":
+        assert torch.allclose(b.float().cpu(), b0 - 1e-3 * a0, rtol=1e-2, atol=1e-2)
+    else:
+        m = 0.9 * c0[:n] + 0.1 * b0
+        v = 0.999 * c0[n:] + 1e-3 * b0 * b0
+        assert torch.allclose(c.cpu()[:n], m, rtol=1e-5, atol=1e-6)
+        assert torch.allclose(c.cpu()[n:], v, rtol=1e-5, atol=1e-6)
+        assert torch.allclose(a.float().cpu(), a0 - 1e-4 * m / (v.sqrt() + 1e-8), rtol=1e-2, atol=1e-2)
+
+
+def test_mix_refuses_overlap():
+    a = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    with pytest.raises(d.DMuonError):
+        d.diag_mix("prep", a, b, a)  # c is a
