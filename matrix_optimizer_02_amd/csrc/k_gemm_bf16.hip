@@ -183,7 +183,9 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wr = wave / C::WC, wc = wave % C::WC;
+    // wave w runs on SIMD w % 4; with wr = w % 2, wc = w / 2 the waves holding
+    // one half of the tile's columns (the epilogue's pieces) sit on all four
+    const int wr = wave % 2, wc = wave / 2;
 
     // ---- this workgroup's queue ------------------------------------------------------
     const int x = (int)(blockIdx.x % kXcds);
@@ -463,7 +465,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         asm volatile("" : "+s"(es));
         const GemmSeg& sg = args.seg[es];
         const int plan_idx = sg.plan_base + ti.slot;
-        const float first_scale = sg.first_iter ? args.scale[plan_idx] : 1.0f;
+        // a scalar load: a vector load here would make the compiler wait for
+        // every load in flight, the next tile's slab included
+        typedef const __attribute__((address_space(4))) float cfloat_t;
+        const float first_scale = sg.first_iter ? *(cfloat_t*)(uintptr_t)(args.scale + plan_idx) : 1.0f;
         if (PHASE == kBX) {
             // Tile rows are long-side indices r, columns short-side indices c:
             // X'[c][r] = s acc[r][c]; E is the X' tile (T rows c, T columns r).
@@ -569,7 +574,16 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             // the queue position of the tile after this one (read once the
             // atomic has returned, at the penultimate slab)
             uint32_t taken = 0;
-            if (tid == 0) taken = atomicAdd(args.queue + x, 1u);
+            if (tid == 0) {
+                // the index through a vector register: otherwise the compiler
+                // turns the one-lane atomic into a wave-wide one whose result it
+                // needs (and waits for, with every load in flight) right away.
+                // The pointer itself keeps its global address space: a flat
+                // atomic would also hold up every LDS wait until it returns.
+                int qx = x;
+                asm volatile("" : "+v"(qx));
+                taken = atomicAdd(args.queue + qx, 1u);
+            }
             #pragma unroll
             for (int i = 0; i < C::FI; ++i)
                 #pragma unroll
@@ -601,6 +615,9 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             // through the last slab and the epilogue.
             DMUON_KSTEPS(L, (KT - 1) * kBK, stage(KT - 2), stage(KT - 1));
             wait_vm<0>();
+            // every wave passes the atomic's result through here, so that the
+            // compiler's wait for it sits here, after this full wait, on every path
+            asm volatile("" : "+v"(taken));
             if (tid == 0) s_next = wgs_x + (int)taken;
             __syncthreads();
             const int kn = __builtin_amdgcn_readfirstlane(s_next);  // wave-uniform
