@@ -31,13 +31,15 @@
 // SIMD and one wave's fragment reads and loads overlap the other's MFMAs).
 // T = 128: 4 waves in a 2 x 2 grid, each 64 x 64.  Every output element is
 // accumulated by one wave in the same k order either way.  K is staged
-// through LDS in 64-deep slabs, two
-// stages, by direct global->LDS loads; 16-byte chunks are XOR-swizzled by row
-// so that the fragment reads hit distinct banks.  Each MFMA k-step is its own
-// scheduling region: its MFMAs interleaved with the next k-step's fragment
-// reads and with a piece of the next slab's loads.  Every epilogue stages the
-// output tile through LDS, so that global reads and writes are whole 16-byte
-// chunks of rows.
+// through LDS in 64-deep slabs by direct global->LDS loads, the P operand in
+// two buffers and the Q operand in three: while slab s is multiplied, P of
+// slab s + 1 and Q of slab s + 2 load (the five buffers take the CU's whole
+// 160 KB for T = 256).  16-byte chunks are XOR-swizzled by row so that the
+// fragment reads hit distinct banks.  Each MFMA k-step is its own scheduling
+// region: its MFMAs interleaved with the next k-step's fragment reads and
+// with half of one operand's later slab.  Every epilogue stages the output
+// tile through LDS, so that global reads and writes are whole 16-byte chunks
+// of rows.
 #include "kcommon.h"
 #include "launch.h"
 #include "tile_map.h"
@@ -95,7 +97,7 @@ struct TileCfg {
     static constexpr int kPRowBytes = 2 * T;
     static constexpr int kPChunks = kPRowBytes / 16;
     static constexpr int kPDmaRows = 1024 / kPRowBytes;
-    // epilogue tile: T rows of T bf16, staged through one stage in kEHalves pieces
+    // epilogue tile: T rows of T bf16, staged through two operand buffers in kEHalves pieces
     static constexpr int kERowBytes = 2 * T;
     static constexpr int kEChunks = T / 8;
     static constexpr int kEHalves = T * kERowBytes / kStageBytes;
@@ -112,7 +114,7 @@ __device__ __forceinline__ void wait_vm() {
 // One wave-wide direct load: 64 lanes x 16 bytes from global memory into the
 // 1 KB of LDS at byte offset lds (wave-uniform), lane l's bytes landing at
 // lds + 16 l.  Written as inline assembly so that the compiler, which cannot
-// tell the two slab stages apart, does not make every later LDS read wait for
+// tell the slab buffers apart, does not make every later LDS read wait for
 // it: the kernel orders these loads itself, with explicit waits and barriers.
 // Every direct load of the kernel goes through here, so the compiler never
 // holds a value of its own in M0.
@@ -168,18 +170,18 @@ struct LoadPlan {
 // workgroup of XCD x starts with that XCD's k-th tile and then takes the next
 // untaken one, counted by the XCD's counter (so tiles of one XCD run in
 // their dealt order, longest segments first).  Consecutive tiles of a
-// workgroup overlap: the last slab of a tile loads the next tile's first
-// slab into the stage it has finished with, and the epilogue stages the
-// output through the other stage, so the next tile's loads are in flight
+// workgroup overlap: the last two slabs of a tile load the next tile's first
+// P slab and first two Q slabs, and the epilogue stages the output through
+// the buffers of the tile's last slab, so the next tile's loads are in flight
 // while the output is written, and its stores drain while the next tile
 // runs.  Every output element is still accumulated by one wave in one k
 // order, so results do not depend on which workgroup takes which tile.
 template <int T, int PHASE>
 __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStageBytes];
-    __shared__ int s_next;  // queue position of this workgroup's next tile
-    static_assert(C::kEHalves * C::kStageBytes == T * C::kERowBytes, "epilogue pieces fill one stage each");
+    // P buffers 0, 1, then Q buffers 0, 1, 2, kOperandBytes each
+    __shared__ __attribute__((aligned(1024))) char smem[5 * C::kOperandBytes];
+    static_assert(C::kEHalves * C::kStageBytes == T * C::kERowBytes, "epilogue pieces fill two buffers each");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -286,25 +288,33 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             if (lp.k_rot >= lp.K) lp.k_rot -= lp.K;
         }
     };
-    // Loads i0 .. i1-1 (of kDmaPerOp per operand) of the slab at loop position
-    // k0 of the tile lp describes into the stage at dst.
-    auto dma_part = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+    // Loads i0 .. i1-1 (of kDmaPerOp) of the P or Q slab at loop position k0
+    // of the tile lp describes into the buffer at dst.
+    auto rot = [&](const LoadPlan& lp, int32_t k0) {
         k0 += lp.k_rot;
-        if (k0 >= lp.K) k0 -= lp.K;
+        return k0 >= lp.K ? k0 - lp.K : k0;
+    };
+    auto dma_p = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+        const char* base = lp.p_base + (int64_t)rot(lp, k0) * lp.p_k;
         #pragma unroll
         for (int i = i0; i < i1; ++i) {
             const int q = wave * C::kDmaPerOp + i;  // 1 KB block of the operand slab
-            dma16(lp.p_base + (int64_t)k0 * lp.p_k + (int64_t)q * lp.p_q, lp.voff_p[i & 1], lds_offset(dst + q * 1024));
-            dma16(lp.q_base + 2 * (int64_t)k0 + (int64_t)q * lp.q_q, lp.voff_q[i & 1],
-                  lds_offset(dst + C::kOperandBytes + q * 1024));
+            dma16(base + (int64_t)q * lp.p_q, lp.voff_p[i & 1], lds_offset(dst + q * 1024));
         }
     };
-    // A slab's loads go out in three pieces: the first right after the barrier
-    // that frees its stage, the other two inside the next two k-steps, so the
+    auto dma_q = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+        const char* base = lp.q_base + 2 * (int64_t)rot(lp, k0);
+        #pragma unroll
+        for (int i = i0; i < i1; ++i) {
+            const int q = wave * C::kDmaPerOp + i;
+            dma16(base + (int64_t)q * lp.q_q, lp.voff_q[i & 1], lds_offset(dst + q * 1024));
+        }
+    };
+    // A slab's loads go out in halves, one per scheduling region (P's in the
+    // region after the barrier and in k-step 0, Q's in k-steps 1 and 2), so the
     // address unit never takes a whole slab's loads at once while the matrix
     // pipe waits behind them.
-    constexpr int kPiece1 = DMUON_SPREAD ? (C::kPiece1Eighths * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
-    constexpr int kPiece2 = DMUON_SPREAD ? (C::kPiece2Eighths * C::kDmaPerOp + 7) / 8 : C::kDmaPerOp;
+    constexpr int kHalf = C::kDmaPerOp / 2;
 
     floatx16 acc[C::FI][C::FJ];
     const int lrow = lane & 31, khalf = lane >> 5;
@@ -341,13 +351,12 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 fa[BUF][i_] = *reinterpret_cast<const bf16x8*>((BASE) + a_row0 + i_ * 32 * kRowBytes + pc_); \
         }                                                                                         \
     } while (0)
-#define DMUON_READ(BUF, BASE, KS_)                                                                \
+#define DMUON_READ(BUF, PB, QB, KS_)                                                              \
     do {                                                                                          \
-        DMUON_READ_A(BUF, BASE, KS_);                                                             \
+        DMUON_READ_A(BUF, PB, KS_);                                                               \
         const int pc_ = ((((KS_) * 2 + khalf) ^ swz) << 4);                                       \
         _Pragma("unroll") for (int j_ = 0; j_ < C::FJ; ++j_)                                      \
-            fb[BUF][j_] = *reinterpret_cast<const bf16x8*>((BASE) + C::kOperandBytes + b_row0 +     \
-                                                           j_ * 32 * kRowBytes + pc_);            \
+            fb[BUF][j_] = *reinterpret_cast<const bf16x8*>((QB) + b_row0 + j_ * 32 * kRowBytes + pc_); \
     } while (0)
 #define DMUON_MFMA(BUF)                                                                           \
     do {                                                                                          \
@@ -359,8 +368,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
 
     constexpr int NREAD = (PHASE == kBX ? 2 : 1) * C::FI + C::FJ;  // fragment reads per k-step
     constexpr int NMFMA = C::FI * C::FJ;                          // MFMAs per k-step
-    constexpr int NV1 = 2 * (kPiece2 - kPiece1);          // loads of piece 1 (k-step 0)
-    constexpr int NV2 = 2 * (C::kDmaPerOp - kPiece2);     // loads of piece 2 (k-step 1)
+    constexpr int NV = kHalf;                                     // loads per region
     // One k-step as its own scheduling region: each of the first MFMAs is
     // followed by one fragment read for the next k-step (and, where the region
     // carries a piece of a slab's loads, by one of those), so the reads are in
@@ -377,19 +385,14 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         if ((NV) > NMFMA) __builtin_amdgcn_sched_group_barrier(0x010, (NV) - NMFMA, 0);           \
         __builtin_amdgcn_sched_barrier(0);                                                        \
     } while (0)
-    // The first KS - 1 k-steps of the slab in stage CUR; pieces 1 and 2 of the
-    // slab at k0 = K0_ of the tile LP_ go into stage OTH during the first two.
-#define DMUON_KSTEPS(LP_, K0_, CUR, OTH)                                                          \
+    // k-step KS_ (0 .. KS - 2) of the slab in buffers PB_, QB_: the MFMAs of
+    // k-step KS_, the fragment reads of k-step KS_ + 1 and the loads LD_.
+#define DMUON_KSTEP(KS_, PB_, QB_, LD_)                                                           \
     do {                                                                                          \
-        _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                                   \
-            if (ks == 0) dma_part(LP_, K0_, OTH, kPiece1, kPiece2);                               \
-            if (ks == 1) dma_part(LP_, K0_, OTH, kPiece2, C::kDmaPerOp);                          \
-            DMUON_READ((ks + 1) & 1, CUR, ks + 1);                                                \
-            DMUON_MFMA(ks & 1);                                                                   \
-            if (ks == 0) DMUON_INTERLEAVE(NV1);                                                   \
-            else if (ks == 1) DMUON_INTERLEAVE(NV2);                                              \
-            else DMUON_INTERLEAVE(0);                                                             \
-        }                                                                                         \
+        LD_;                                                                                      \
+        DMUON_READ(((KS_) + 1) & 1, PB_, QB_, (KS_) + 1);                                         \
+        DMUON_MFMA((KS_) & 1);                                                                    \
+        DMUON_INTERLEAVE(NV);                                                                     \
     } while (0)
 
     // ---- epilogue ---------------------------------------------------------------------
@@ -397,37 +400,49 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     //                  and column  wc*CW + 32 j + lane % 32   of the T x T tile,
     // i.e. four consecutive rows r0 .. r0 + 3 of one column c per (i, j, v / 4).
     // The tile goes through LDS transposed, as E[c][r] = C[r][c]: each lane's
-    // four values are one 8-byte piece of a row of E.  E is staged through one
-    // stage in kEHalves pieces of kERows rows (columns c) each, the waves
-    // holding a piece's columns writing it.
+    // four values are one 8-byte piece of a row of E.  E is staged through the
+    // last slab's two buffers in kEHalves pieces of kERows rows (columns c)
+    // each, the waves holding a piece's columns writing it.
     constexpr int kERows = T / C::kEHalves;
     const int my_piece = (wc * C::CW) / kERows;
+    // E lives in two buffers of kOperandBytes (the P and Q buffers of the
+    // tile's last slab): rows 0 .. kERegRows - 1 in the first, the rest in the
+    // second.
+    constexpr int kERegRows = C::kOperandBytes / C::kERowBytes;
+    static_assert(2 * kERegRows == kERows, "a piece of E fills the two buffers");
+    struct EBuf {
+        char* a;
+        char* b;
+    };
+    auto erow = [&](const EBuf& E, int c) -> char* {
+        return (c < kERegRows ? E.a : E.b) + (c & (kERegRows - 1)) * C::kERowBytes;
+    };
     // kERows rows of 2 T bytes from global (row stride ld elements) into E, whole.
-    auto load_piece = [&](int eln, char* ebuf, const uint16_t* src, int64_t ld) {
+    auto load_piece = [&](int eln, const EBuf& ebuf, const uint16_t* src, int64_t ld) {
         constexpr int kLoads = kERows * C::kERowBytes / 1024 / C::NW;  // 1 KB loads per wave
         #pragma unroll 8
         for (int i = 0; i < kLoads; ++i) {
             const int q = wave * kLoads + i;
             const int row = (1024 / C::kERowBytes) * q + eln / C::kEChunks;
             const int lc = (eln % C::kEChunks) ^ swizzle_e<T>(row);
-            dma16(src + row * ld + lc * 8, lds_offset(ebuf + q * 1024));
+            // the 1 KB block q holds whole E rows, all in one of E's two buffers
+            dma16(src + row * ld + lc * 8, lds_offset(erow(ebuf, (1024 / C::kERowBytes) * q)));
         }
         wait_vm<0>();
         __syncthreads();
     };
     // E row c, columns r .. r + 3 (r a multiple of 4)
-    auto e_ptr = [&](char* ebuf, int c, int r) -> char* {
-        return ebuf + c * C::kERowBytes + (((r >> 3) ^ swizzle_e<T>(c)) << 4) + (r & 7) * 2;
+    auto e_ptr = [&](const EBuf& ebuf, int c, int r) -> char* {
+        return erow(ebuf, c) + (((r >> 3) ^ swizzle_e<T>(c)) << 4) + (r & 7) * 2;
     };
     // E rows to global rows (row stride ld elements), whole 16-byte chunks.
-    auto store_rows = [&](int etid, char* ebuf, uint16_t* dst, int64_t ld) {
+    auto store_rows = [&](int etid, const EBuf& ebuf, uint16_t* dst, int64_t ld) {
         constexpr int kStores = kERows * C::kEChunks / C::NT;
         #pragma unroll 8
         for (int i = 0; i < kStores; ++i) {
             const int q = etid + C::NT * i;
             const int row = q / C::kEChunks, lc = q % C::kEChunks;
-            const uint4 v = *reinterpret_cast<const uint4*>(ebuf + row * C::kERowBytes +
-                                                            ((lc ^ swizzle_e<T>(row)) << 4));
+            const uint4 v = *reinterpret_cast<const uint4*>(erow(ebuf, row) + ((lc ^ swizzle_e<T>(row)) << 4));
             *reinterpret_cast<uint4*>(dst + row * ld + lc * 8) = v;
         }
     };
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     // r0 + 4 q .. + 3) and hands lane i the four values E[c0 .. c0 + 3][r0 + i];
     // two such reads give a lane 8 consecutive c of one r.  A wave covers 16
     // rows r and 32 columns c per store, the 4 groups taking 8 columns each.
-    auto store_cols = [&](int eln, char* ebuf, uint16_t* dst, int64_t ld) {
+    auto store_cols = [&](int eln, const EBuf& ebuf, uint16_t* dst, int64_t ld) {
         const int g = eln >> 4, i16 = eln & 15, k = i16 >> 2, q = i16 & 3;
         constexpr int kRowBlocks = T / 16, kColBlocks = kERows / 32;
         #pragma unroll 4
@@ -453,7 +468,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             *reinterpret_cast<shortx8*>(dst + (int64_t)(r0 + i16) * ld + cb) = v;
         }
     };
-    auto epilogue = [&](const TileInfo& ti, char* ebuf) {
+    auto epilogue = [&](const TileInfo& ti, const EBuf& ebuf) {
         // Lane indices passed through an empty asm statement: the epilogue's
         // per-lane addresses are then computed here, once per tile, rather
         // than hoisted out of the tile loop into registers the main loop needs.
@@ -558,21 +573,39 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     };
 
     // ---- the tiles of this workgroup ------------------------------------------------------
+    // Slab g of the workgroup (counted across its tiles) has its P operand in
+    // P buffer g % 2 and its Q operand in Q buffer g % 3.  While slab s of a
+    // tile is multiplied, its P of slab s + 1 and its Q of slab s + 2 load,
+    // into the buffers slabs s - 1 and s - 1 have left: P's halves in the
+    // region after the barrier and in k-step 0, Q's in k-steps 1 and 2.  The
+    // end of slab s waits for slab s + 1 (P issued in this slab, Q in the one
+    // before): loads complete in issue order, so waiting until at most the
+    // kDmaPerOp Q loads of slab s + 2 are in flight lands it (stores in between
+    // only make such a wait longer).  Past the tile's end these loads are the
+    // next tile's: Q of its slab 0 in slab KT - 2, P of slab 0 and Q of slab 1
+    // in slab KT - 1.  The next tile is read from the queue at the end of slab
+    // KT - 3 (at the tile's start when it has two slabs), through the Q buffer
+    // that slab has left and its next tile's Q loads will fill, and its loads
+    // are planned in slab KT - 2, after this tile's last P loads.
+    auto pbuf = [&](int b) { return smem + b * C::kOperandBytes; };
+    auto qbuf = [&](int b) { return smem + (2 + b) * C::kOperandBytes; };
+    auto next3 = [](int b) { return b == 2 ? 0 : b + 1; };
     int kq = (int)(blockIdx.x / kXcds);  // this workgroup's first tile of its XCD's queue
     if (kq < count_x) {
         TileInfo cur;
         decode(kq, cur);
         LoadPlan L;
         plan_loads(cur, L);
-        // prologue: slab 0 whole and the first piece of slab 1; wait for slab 0
-        dma_part(L, 0, smem, 0, C::kDmaPerOp);
-        dma_part(L, kBK, smem + C::kStageBytes, 0, kPiece1);
-        wait_vm<2 * kPiece1>();
+        int gp = 0, gq = 0;  // the current slab's P and Q buffers
+        // prologue: P and Q of slab 0, Q of slab 1; wait for slab 0
+        dma_p(L, 0, pbuf(0), 0, C::kDmaPerOp);
+        dma_q(L, 0, qbuf(0), 0, C::kDmaPerOp);
+        dma_q(L, kBK, qbuf(1), 0, C::kDmaPerOp);
+        wait_vm<C::kDmaPerOp>();
         __syncthreads();
-        int par = 0;  // slab kt of the current tile sits in stage (kt + par) & 1
         for (;;) {
-            // the queue position of the tile after this one (read once the
-            // atomic has returned, at the penultimate slab)
+            // the queue position of the tile after this one; its value is used
+            // only in slab KT - 2 (the compiler waits for it there)
             uint32_t taken = 0;
             if (tid == 0) {
                 // the index through a vector register: otherwise the compiler
@@ -590,69 +623,74 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 for (int j = 0; j < C::FJ; ++j)
                     #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-            auto stage = [&](int kt) { return smem + ((kt + par) & 1) * C::kStageBytes; };
             const int KT = (int)(L.K / kBK);  // >= 2: K is a multiple of the tile
-            DMUON_READ(0, stage(0), 0);
-            // Slab kt (not one of the last two): pieces 1 and 2 of slab kt + 1 go
-            // into its stage during the first two k-steps.  The last k-step waits
-            // for slab kt + 1 (nothing else is in flight then); the barrier
-            // publishes every wave's share of it and makes sure every wave is done
-            // reading slab kt's stage, which then takes the first piece of slab kt + 2.
-            for (int kt = 0; kt + 2 < KT; ++kt) {
-                DMUON_KSTEPS(L, (kt + 1) * kBK, stage(kt), stage(kt + 1));
-                wait_vm<0>();
-                __syncthreads();
-                __builtin_amdgcn_sched_barrier(0);
-                dma_part(L, (kt + 2) * kBK, stage(kt), 0, kPiece1);
-                __builtin_amdgcn_sched_barrier(0);
-                DMUON_READ(0, stage(kt + 1), 0);
-                DMUON_MFMA((KS - 1) & 1);
-                DMUON_INTERLEAVE(0);
-            }
-            // The penultimate slab: its stage, once free, takes the next tile's
-            // slab 0 whole (this tile's slab 0 again, if there is no next tile:
-            // harmless loads into a stage nothing reads any more), in flight
-            // through the last slab and the epilogue.
-            DMUON_KSTEPS(L, (KT - 1) * kBK, stage(KT - 2), stage(KT - 1));
-            wait_vm<0>();
-            // every wave passes the atomic's result through here, so that the
-            // compiler's wait for it sits here, after this full wait, on every path
-            asm volatile("" : "+v"(taken));
-            if (tid == 0) s_next = wgs_x + (int)taken;
-            __syncthreads();
-            const int kn = __builtin_amdgcn_readfirstlane(s_next);  // wave-uniform
-            const bool has_next = kn < count_x;
+            bool has_next = false;
             TileInfo nxt = cur;
-            if (has_next) decode(kn, nxt);
-            plan_loads(nxt, L);  // this tile's plan is not needed any more
+            // The next tile, from the queue: every wave passes the atomic's
+            // result through the empty asm (so that the compiler's wait for it
+            // sits here on every path), thread 0 posts it in the free Q buffer
+            // mail, and the buffer takes no loads before every wave has read it.
+            auto next_tile = [&](char* mail) {
+                asm volatile("" : "+v"(taken));
+                if (tid == 0) *reinterpret_cast<int*>(mail) = wgs_x + (int)taken;
+                __syncthreads();
+                const int kn = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(mail));
+                __syncthreads();
+                has_next = kn < count_x;
+                if (has_next) decode(kn, nxt);
+            };
+            if (KT == 2) next_tile(qbuf(next3(next3(gq))));
+            // region after the barrier of slab 0: half of P of slab 1 (this tile's:
+            // K covers at least two slabs), k-step 0 fragments
             __builtin_amdgcn_sched_barrier(0);
-            dma_part(L, 0, stage(KT - 2), 0, C::kDmaPerOp);
-            __builtin_amdgcn_sched_barrier(0);
-            DMUON_READ(0, stage(KT - 1), 0);
-            DMUON_MFMA((KS - 1) & 1);
-            DMUON_INTERLEAVE(0);
-            // the last slab
-            _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {
-                DMUON_READ((ks + 1) & 1, stage(KT - 1), ks + 1);
-                DMUON_MFMA(ks & 1);
-                DMUON_INTERLEAVE(0);
+            dma_p(L, kBK, pbuf(gp ^ 1), 0, kHalf);
+            DMUON_READ(0, pbuf(gp), qbuf(gq), 0);
+            DMUON_INTERLEAVE(NV);
+            for (int kt = 0;; ++kt) {
+                char* const pb = pbuf(gp);
+                char* const qb = qbuf(gq);
+                // P of slab kt + 1 (the next tile's slab 0 at the tile's last slab)
+                const int32_t kp = kt + 1 < KT ? (kt + 1) * kBK : 0;
+                DMUON_KSTEP(0, pb, qb, dma_p(L, kp, pbuf(gp ^ 1), kHalf, C::kDmaPerOp));
+                if (kt + 2 == KT) plan_loads(nxt, L);  // this tile's loads are all issued
+                // Q of slab kt + 2 (past the end: the next tile's slab 0 or 1)
+                const int32_t kqo = (kt + 2 < KT ? kt + 2 : kt + 2 - KT) * kBK;
+                char* const qd = qbuf(next3(next3(gq)));
+                DMUON_KSTEP(1, pb, qb, dma_q(L, kqo, qd, 0, kHalf));
+                DMUON_KSTEP(2, pb, qb, dma_q(L, kqo, qd, kHalf, C::kDmaPerOp));
+                if (kt + 1 == KT) break;
+                wait_vm<C::kDmaPerOp>();  // slab kt + 1 (Q of slab kt + 2 may be in flight)
+                __syncthreads();
+                if (kt + 3 == KT) next_tile(qb);  // slab kt's Q buffer takes the next tile's slab 0
+                gp ^= 1;
+                gq = next3(gq);
+                // the region after the barrier: half of P of slab kt + 2 (the next
+                // tile's slab 0 when kt + 2 is this tile's end), slab kt + 1's k-step
+                // 0 fragments, slab kt's k-step 3 MFMAs
+                const int32_t kp2 = kt + 2 < KT ? (kt + 2) * kBK : 0;
+                __builtin_amdgcn_sched_barrier(0);
+                dma_p(L, kp2, pbuf(gp ^ 1), 0, kHalf);
+                DMUON_READ(0, pbuf(gp), qbuf(gq), 0);
+                DMUON_MFMA((KS - 1) & 1);
+                DMUON_INTERLEAVE(NV);
             }
-            DMUON_MFMA((KS - 1) & 1);
-            __syncthreads();  // every wave is done with the last slab's stage
-            epilogue(cur, stage(KT - 1));
+            DMUON_MFMA((KS - 1) & 1);  // the last slab's k-step 3
+            __syncthreads();           // every wave is done with the last slab's buffers
+            epilogue(cur, EBuf{pbuf(gp), qbuf(gq)});
             if (!has_next) break;
-            // The next tile: its slab 0 sits in stage (KT - 2 + par) & 1, complete
-            // (every wave waited for its share before the epilogue's first stores,
-            // and the epilogue's barriers published it); slab 1's first piece goes
-            // into the stage the epilogue has finished with.  The epilogue's
+            // The next tile: P of its slab 0 and Q of its slabs 0 and 1 were issued
+            // in this tile's last two slabs; slab 0 is waited for (Q of slab 1 and
+            // the epilogue's stores may be in flight) and published.  The epilogue's
             // stores drain while the next tile runs.
             __syncthreads();
-            par = (KT + par) & 1;
+            wait_vm<C::kDmaPerOp>();
+            __syncthreads();
+            gp ^= 1;
+            gq = next3(gq);
             cur = nxt;
-            dma_part(L, kBK, stage(1), 0, kPiece1);
         }
     }
-#undef DMUON_KSTEPS
+#undef DMUON_KSTEP
 #undef DMUON_INTERLEAVE
 #undef DMUON_READ
 #undef DMUON_READ_A
@@ -670,7 +708,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
 }
 
 // Workgroups per XCD of a persistent launch: one per CU for 256-tiles (their
-// two 64 KB stages fill a CU's LDS), two per CU for 128-tiles; never more than
+// five 32 KB operand buffers fill a CU's LDS), two per CU for 128-tiles; never more than
 // the XCD has tiles.
 template <int T>
 int persistent_grid(int tiles) {
