@@ -44,6 +44,8 @@
 #include "launch.h"
 #include "tile_map.h"
 
+#include <cmath>
+
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
 #endif
@@ -57,9 +59,6 @@
 #endif
 #ifndef DMUON_PIECE2
 #define DMUON_PIECE2 -1
-#endif
-#ifndef DMUON_ROTATE_K
-#define DMUON_ROTATE_K 1
 #endif
 
 namespace dmuon {
@@ -176,7 +175,7 @@ struct LoadPlan {
 // while the output is written, and its stores drain while the next tile
 // runs.  Every output element is still accumulated by one wave in one k
 // order, so results do not depend on which workgroup takes which tile.
-template <int T, int PHASE>
+template <int T, int PHASE, bool FOLD>
 __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
     // P buffers 0, 1, then Q buffers 0, 1, 2, kOperandBytes each
@@ -278,12 +277,12 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         lp.p_q = PHASE == kBX ? 2 * C::kPDmaRows * (int32_t)sg.n_pad : 16 * ldq;
         lp.q_q = 16 * ldq;
         lp.K = ldq;
-        // The square's K loop starts right after the T-wide k range that its
-        // epilogue reads back (A columns I T .., the mirrored A block), so that
-        // range is loaded last and the epilogue finds it in L2.  K is a multiple
-        // of T.
+        // The square's K loop starts right after block I of k (A columns I T ..),
+        // so that the tile's last T / kBK slabs are that block: the folded b A
+        // term reads it there (and the read-back path finds it in L2).  K is a
+        // multiple of T.
         lp.k_rot = 0;
-        if (DMUON_ROTATE_K && PHASE == kSquare) {
+        if (PHASE == kSquare) {
             lp.k_rot = (ti.I + 1) * T;
             if (lp.k_rot >= lp.K) lp.k_rot -= lp.K;
         }
@@ -318,6 +317,19 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
 
     floatx16 acc[C::FI][C::FJ];
     const int lrow = lane & 31, khalf = lane >> 5;
+    // The square's b A term, folded into the accumulators: B' = c (A A^T +
+    // (b / c) A) + a I.  K is rotated so that the tile's last T / kBK slabs are
+    // block I of k, where Q's fragments are A[J T + c][I T + k'] = A[I T + k'][J T + c]
+    // (A is symmetric); one more MFMA per fragment against (b / c) times the
+    // identity (rows k' of the tile) adds (b / c) A[I T + r][J T + c] to
+    // acc[r][c].  b / c goes in as two bf16 parts, so it keeps about 16 bits.
+    // FOLD (the launch takes it when c != 0 and |b / c| <= 64; the quintic's
+    // b / c is -2.35): for other coefficients the epilogue reads A's block back
+    // instead, in a kernel of its own.
+    constexpr bool sq_fold = PHASE == kSquare && FOLD;
+    const float sq_bc = sq_fold ? args.b / args.c : 0.f;
+    const __bf16 sq_hi = (__bf16)sq_bc;
+    const __bf16 sq_lo = (__bf16)(sq_bc - (float)sq_hi);
     const int swz = swizzle(lrow);  // fragment rows start at multiples of 32
     const int a_row0 = (wr * C::RW + lrow) * kRowBytes;
     const int b_row0 = (wc * C::CW + lrow) * kRowBytes;
@@ -384,6 +396,34 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         if (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);         \
         if ((NV) > NMFMA) __builtin_amdgcn_sched_group_barrier(0x010, (NV) - NMFMA, 0);           \
         __builtin_amdgcn_sched_barrier(0);                                                        \
+    } while (0)
+    // The folded b A term for k-step KS_ of slab KT_ (Q's fragments in fb[BUF_]):
+    // k' = 16 KS_ + (position of the slab in block I) kBK + the lane's 8 k;
+    // rows r of the tile with r = k' get (b / c) on the diagonal of the
+    // identity fragment, in the 32-row fragment i that holds them.
+#define DMUON_SQ_FOLD(KT_, KS_, BUF_)                                                             \
+    do {                                                                                          \
+        if (sq_fold) {                                                                            \
+            const int sp_ = (KT_) - (KT - T / kBK);                                               \
+            const int g_ = sp_ * kBK + 16 * (KS_) - wr * C::RW;  /* rows of this k-step, wave-relative */ \
+            if (sp_ >= 0 && g_ >= 0 && g_ < C::RW) {                                              \
+                const int i0_ = g_ >> 5;                                                          \
+                const int d_ = lrow + 32 * i0_ - g_ - 8 * khalf;                                  \
+                bf16x8 hi_, lo_;                                                                  \
+                _Pragma("unroll") for (int e_ = 0; e_ < 8; ++e_) {                                \
+                    hi_[e_] = d_ == e_ ? sq_hi : (__bf16)0.f;                                     \
+                    lo_[e_] = d_ == e_ ? sq_lo : (__bf16)0.f;                                     \
+                }                                                                                 \
+                _Pragma("unroll") for (int i_ = 0; i_ < C::FI; ++i_) {                            \
+                    if (i_ == i0_) {                                                              \
+                        _Pragma("unroll") for (int j_ = 0; j_ < C::FJ; ++j_) {                    \
+                            acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi_, fb[BUF_][j_], acc[i_][j_], 0, 0, 0); \
+                            acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo_, fb[BUF_][j_], acc[i_][j_], 0, 0, 0); \
+                        }                                                                         \
+                    }                                                                             \
+                }                                                                                 \
+            }                                                                                     \
+        }                                                                                         \
     } while (0)
     // k-step KS_ (0 .. KS - 2) of the slab in buffers PB_, QB_: the MFMAs of
     // k-step KS_, the fragment reads of k-step KS_ + 1 and the loads LD_.
@@ -509,7 +549,6 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                                 *reinterpret_cast<uint2*>(e_ptr(ebuf, c, r0)) = o;
                             }
                 }
-                if (h == 0) wait_vm<0>();  // the next tile's slab 0, before any store is issued
                 __syncthreads();
                 store_rows(etid, ebuf, Xd + (int64_t)h * kERows * ldn, ldn);
                 if (h + 1 < C::kEHalves) __syncthreads();  // before the next piece overwrites E
@@ -526,7 +565,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             const float beta = args.b;
             #pragma unroll
             for (int h = 0; h < C::kEHalves; ++h) {
-                if (PHASE == kSquare)
+                if (PHASE == kSquare && !sq_fold)
                     load_piece(eln, ebuf,
                                reinterpret_cast<const uint16_t*>(args.ws + sg.p_off + ti.slot * sg.a_stride) +
                                    ((int64_t)ti.J * T + h * kERows) * ld + (int64_t)ti.I * T,
@@ -545,11 +584,13 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                                 #pragma unroll
                                 for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][4 * v4 + e];
                                 if (PHASE == kSquare) {
-                                    const uint2 xa = *reinterpret_cast<const uint2*>(p);
-                                    v[0] = fmaf(beta, __uint_as_float(xa.x << 16), v[0]);
-                                    v[1] = fmaf(beta, __uint_as_float(xa.x & 0xffff0000u), v[1]);
-                                    v[2] = fmaf(beta, __uint_as_float(xa.y << 16), v[2]);
-                                    v[3] = fmaf(beta, __uint_as_float(xa.y & 0xffff0000u), v[3]);
+                                    if (!sq_fold) {
+                                        const uint2 xa = *reinterpret_cast<const uint2*>(p);
+                                        v[0] = fmaf(beta, __uint_as_float(xa.x << 16), v[0]);
+                                        v[1] = fmaf(beta, __uint_as_float(xa.x & 0xffff0000u), v[1]);
+                                        v[2] = fmaf(beta, __uint_as_float(xa.y << 16), v[2]);
+                                        v[3] = fmaf(beta, __uint_as_float(xa.y & 0xffff0000u), v[3]);
+                                    }
                                     if (ti.I == ti.J) {  // the a I term on the diagonal
                                         #pragma unroll
                                         for (int e = 0; e < 4; ++e)
@@ -562,7 +603,6 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                                 *reinterpret_cast<uint2*>(p) = o;
                             }
                 }
-                if (h == 0) wait_vm<0>();  // the next tile's slab 0, before any store is issued
                 __syncthreads();
                 store_rows(etid, ebuf, Out + ((int64_t)ti.J * T + h * kERows) * ld + (int64_t)ti.I * T, ld);
                 if (ti.I != ti.J)
@@ -652,12 +692,15 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 // P of slab kt + 1 (the next tile's slab 0 at the tile's last slab)
                 const int32_t kp = kt + 1 < KT ? (kt + 1) * kBK : 0;
                 DMUON_KSTEP(0, pb, qb, dma_p(L, kp, pbuf(gp ^ 1), kHalf, C::kDmaPerOp));
+                DMUON_SQ_FOLD(kt, 0, 0);
                 if (kt + 2 == KT) plan_loads(nxt, L);  // this tile's loads are all issued
                 // Q of slab kt + 2 (past the end: the next tile's slab 0 or 1)
                 const int32_t kqo = (kt + 2 < KT ? kt + 2 : kt + 2 - KT) * kBK;
                 char* const qd = qbuf(next3(next3(gq)));
                 DMUON_KSTEP(1, pb, qb, dma_q(L, kqo, qd, 0, kHalf));
+                DMUON_SQ_FOLD(kt, 1, 1);
                 DMUON_KSTEP(2, pb, qb, dma_q(L, kqo, qd, kHalf, C::kDmaPerOp));
+                DMUON_SQ_FOLD(kt, 2, 0);
                 if (kt + 1 == KT) break;
                 wait_vm<C::kDmaPerOp>();  // slab kt + 1 (Q of slab kt + 2 may be in flight)
                 __syncthreads();
@@ -673,8 +716,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 DMUON_READ(0, pbuf(gp), qbuf(gq), 0);
                 DMUON_MFMA((KS - 1) & 1);
                 DMUON_INTERLEAVE(NV);
+                DMUON_SQ_FOLD(kt, KS - 1, (KS - 1) & 1);
             }
             DMUON_MFMA((KS - 1) & 1);  // the last slab's k-step 3
+            DMUON_SQ_FOLD(KT - 1, KS - 1, (KS - 1) & 1);
             __syncthreads();           // every wave is done with the last slab's buffers
             epilogue(cur, EBuf{pbuf(gp), qbuf(gq)});
             if (!has_next) break;
@@ -691,6 +736,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         }
     }
 #undef DMUON_KSTEP
+#undef DMUON_SQ_FOLD
 #undef DMUON_INTERLEAVE
 #undef DMUON_READ
 #undef DMUON_READ_A
@@ -720,11 +766,16 @@ int persistent_grid(int tiles) {
 template <int T>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)persistent_grid<T>(a.total_blocks)), block(TileCfg<T>::NT);
+    // the square folds its b A term into the accumulators when b / c is moderate
+    const bool fold = a.c != 0.f && std::fabs(a.b / a.c) <= 64.f;
     switch (a.phase) {
-        case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram>), grid, block, 0, stream, a); break;
-        case kSquare: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare>), grid, block, 0, stream, a); break;
-        case kBX: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX>), grid, block, 0, stream, a); break;
-        case kProd: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kProd>), grid, block, 0, stream, a); break;
+        case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram, true>), grid, block, 0, stream, a); break;
+        case kSquare:
+            if (fold) hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare, false>), grid, block, 0, stream, a);
+            break;
+        case kBX: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX, true>), grid, block, 0, stream, a); break;
+        case kProd: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kProd, true>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -332,6 +332,35 @@ def test_rank_one_and_diagonal_inputs():
         assert e < tol
 
 
+# ---- other coefficients: the square's b A term folded into the accumulators, or read
+# back in the epilogue (c = 0 or |b / c| > 64) ------------------------------------------
+
+OTHER_COEFFS = [(1.5, -0.5, 0.0),          # the cubic iteration: read back
+                (1.5, -0.5, 1e-3),         # |b / c| = 500: read back
+                (3.0, -3.2, 1.2),          # folded
+                (3.4445, -4.7750, 2.0315)]  # the quintic: folded
+OTHER_SHAPES = [(768, 768), (520, 1300), (1300, 520), (1024, 3072), (1, 513), (128, 640)]
+
+
+@pytest.mark.parametrize("algo", ["auto", "short_side"])
+@pytest.mark.parametrize("coeffs", OTHER_COEFFS)
+def test_other_coefficients(coeffs, algo):
+    a, b, c = coeffs
+    w = custom_workload("coeffs", OTHER_SHAPES, "bf16", "bf16", g_std=1.0)
+    Gs = [host_tensor(w, i, GRAD, seed=11) for i in range(w.count)]
+    say(f"case coefficients {coeffs} {algo}")
+    inputs = [g.cuda() for g in Gs]
+    plan = d.plan_for(inputs, [torch.float32] * len(inputs), algo)
+    ws = d.workspace_for(plan)
+    outs = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in inputs]
+    d.ns_orthogonalize_batched(plan, inputs, outs, ns_steps=5, a=a, b=b, c=c, eps=EPS, workspace=ws)
+    torch.cuda.synchronize()
+    for i, g in enumerate(Gs):
+        e = rel(f64(outs[i]), oracle.newton_schulz(f64(g), 5, a, b, c, EPS))
+        say(f"  {OTHER_SHAPES[i]}: rel err {e:.3e}")
+        assert e < TOL["bf16"], (coeffs, OTHER_SHAPES[i], e)
+
+
 # ---- the Gram-space recurrence: restart intervals, conditioning, growth bound ---------
 
 GRAM_SHAPES = [(256, 768), (768, 256), (384, 1000), (128, 640), (72, 200), (512, 1536)]
@@ -383,8 +412,11 @@ def test_gram_space_ill_conditioned_inputs():
 def test_gram_space_growth_bound_falls_back():
     # Beyond |a|^gram_restart = 2^64 a call runs Gram-space buckets on the short
     # side: the same products as a short-side plan, so the same bits.  Below it
-    # the two forms differ (rounding), which shows the Gram space ran.
-    w = custom_workload("fallback", [(256, 768), (384, 128)], "bf16", "bf16", g_std=1.0)
+    # the two forms differ (rounding), which shows the Gram space ran.  Both
+    # shapes run tiled products in either plan (a 128 x n bucket with n <= 512
+    # would run resident in the short-side plan, whose square rounds its b A
+    # term differently).
+    w = custom_workload("fallback", [(256, 768), (640, 128)], "bf16", "bf16", g_std=1.0)
     Gs = [host_tensor(w, i, GRAD, seed=6).cuda() for i in range(w.count)]
     bits = lambda t: t.view(torch.int32)
     over = math.floor(64 / math.log2(A)) + 1
