@@ -84,7 +84,6 @@ struct TileCfg {
     static constexpr int WC = NW / 2;              // waves across the tile's columns (2 down its rows)
     static constexpr int RW = T / 2, CW = T / WC;  // rows, columns of one wave's sub-tile
     static constexpr int FI = RW / 32, FJ = CW / 32;  // MFMA blocks per wave per dim
-    static constexpr int kDmaPerOp = T * kRowBytes / 1024 / NW;  // 1 KB loads per wave per operand per slab
     // A slab's loads in pieces ending at these eighths (measured: with two
     // waves per SIMD, half right after the barrier and half in the first
     // k-step; with one, 3/8, 3/8 and 2/8 over the barrier and two k-steps).
@@ -247,7 +246,13 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     //   (l / 8) ^ (q & 1).
     //   B X P slab (rows k of X): R = 2 (T = 256) or 4, chunk swizzle
     //   swizzle_p of the row, whose two low bits hold 2 (q & 1) + l / 32 or l / 16.
-    static_assert(C::kDmaPerOp % 2 == 0, "load parity");
+    // Waves that issue the slab loads.  In B X, waves 0 .. 3 (one of each pair
+    // sharing a SIMD) issue all of them, so the MFMAs of waves 4 .. 7 never
+    // wait behind loads of their own (B X 1% faster, same box; the other
+    // phases measured 0.6-5.5% slower that way); elsewhere every wave loads.
+    constexpr int kLoaders = PHASE == kBX && C::NW == 8 ? 4 : C::NW;
+    constexpr int kDmaPerOp = T * kRowBytes / 1024 / kLoaders;  // 1 KB loads per loader wave per operand per slab
+    static_assert(kDmaPerOp % 2 == 0, "load parity");
     auto plan_loads = [&](const TileInfo& ti, LoadPlan& lp) {
         const GemmSeg& sg = args.seg[ti.s];
         const int32_t ldq = k_extent(ti);
@@ -294,18 +299,20 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         return k0 >= lp.K ? k0 - lp.K : k0;
     };
     auto dma_p = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+        if (kLoaders < C::NW && wave >= kLoaders) return;
         const char* base = lp.p_base + (int64_t)rot(lp, k0) * lp.p_k;
         #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            const int q = wave * C::kDmaPerOp + i;  // 1 KB block of the operand slab
+            const int q = wave * kDmaPerOp + i;  // 1 KB block of the operand slab
             dma16(base + (int64_t)q * lp.p_q, lp.voff_p[i & 1], lds_offset(dst + q * 1024));
         }
     };
     auto dma_q = [&](const LoadPlan& lp, int32_t k0, char* dst, int i0, int i1) {
+        if (kLoaders < C::NW && wave >= kLoaders) return;
         const char* base = lp.q_base + 2 * (int64_t)rot(lp, k0);
         #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            const int q = wave * C::kDmaPerOp + i;
+            const int q = wave * kDmaPerOp + i;
             dma16(base + (int64_t)q * lp.q_q, lp.voff_q[i & 1], lds_offset(dst + q * 1024));
         }
     };
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     // region after the barrier and in k-step 0, Q's in k-steps 1 and 2), so the
     // address unit never takes a whole slab's loads at once while the matrix
     // pipe waits behind them.
-    constexpr int kHalf = C::kDmaPerOp / 2;
+    constexpr int kHalf = kDmaPerOp / 2;
 
     floatx16 acc[C::FI][C::FJ];
     const int lrow = lane & 31, khalf = lane >> 5;
@@ -380,7 +387,9 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
 
     constexpr int NREAD = (PHASE == kBX ? 2 : 1) * C::FI + C::FJ;  // fragment reads per k-step
     constexpr int NMFMA = C::FI * C::FJ;                          // MFMAs per k-step
-    constexpr int NV = kHalf;                                     // loads per region
+    // loads per region in the MFMAs' scheduling groups (none where they sit
+    // behind the loader waves' branch)
+    constexpr int NV = kLoaders == C::NW ? kHalf : 0;
     // One k-step as its own scheduling region: each of the first MFMAs is
     // followed by one fragment read for the next k-step (and, where the region
     // carries a piece of a slab's loads, by one of those), so the reads are in
@@ -621,7 +630,8 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     // end of slab s waits for slab s + 1 (P issued in this slab, Q in the one
     // before): loads complete in issue order, so waiting until at most the
     // kDmaPerOp Q loads of slab s + 2 are in flight lands it (stores in between
-    // only make such a wait longer).  Past the tile's end these loads are the
+    // only make such a wait longer), and the barrier after it lands it for the
+    // waves that issue no loads.  Past the tile's end these loads are the
     // next tile's: Q of its slab 0 in slab KT - 2, P of slab 0 and Q of slab 1
     // in slab KT - 1.  The next tile is read from the queue at the end of slab
     // KT - 3 (at the tile's start when it has two slabs), through the Q buffer
@@ -638,10 +648,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         plan_loads(cur, L);
         int gp = 0, gq = 0;  // the current slab's P and Q buffers
         // prologue: P and Q of slab 0, Q of slab 1; wait for slab 0
-        dma_p(L, 0, pbuf(0), 0, C::kDmaPerOp);
-        dma_q(L, 0, qbuf(0), 0, C::kDmaPerOp);
-        dma_q(L, kBK, qbuf(1), 0, C::kDmaPerOp);
-        wait_vm<C::kDmaPerOp>();
+        dma_p(L, 0, pbuf(0), 0, kDmaPerOp);
+        dma_q(L, 0, qbuf(0), 0, kDmaPerOp);
+        dma_q(L, kBK, qbuf(1), 0, kDmaPerOp);
+        wait_vm<kDmaPerOp>();
         __syncthreads();
         for (;;) {
             // the queue position of the tile after this one; its value is used
@@ -691,7 +701,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 char* const qb = qbuf(gq);
                 // P of slab kt + 1 (the next tile's slab 0 at the tile's last slab)
                 const int32_t kp = kt + 1 < KT ? (kt + 1) * kBK : 0;
-                DMUON_KSTEP(0, pb, qb, dma_p(L, kp, pbuf(gp ^ 1), kHalf, C::kDmaPerOp));
+                DMUON_KSTEP(0, pb, qb, dma_p(L, kp, pbuf(gp ^ 1), kHalf, kDmaPerOp));
                 DMUON_SQ_FOLD(kt, 0, 0);
                 if (kt + 2 == KT) plan_loads(nxt, L);  // this tile's loads are all issued
                 // Q of slab kt + 2 (past the end: the next tile's slab 0 or 1)
@@ -699,10 +709,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 char* const qd = qbuf(next3(next3(gq)));
                 DMUON_KSTEP(1, pb, qb, dma_q(L, kqo, qd, 0, kHalf));
                 DMUON_SQ_FOLD(kt, 1, 1);
-                DMUON_KSTEP(2, pb, qb, dma_q(L, kqo, qd, kHalf, C::kDmaPerOp));
+                DMUON_KSTEP(2, pb, qb, dma_q(L, kqo, qd, kHalf, kDmaPerOp));
                 DMUON_SQ_FOLD(kt, 2, 0);
                 if (kt + 1 == KT) break;
-                wait_vm<C::kDmaPerOp>();  // slab kt + 1 (Q of slab kt + 2 may be in flight)
+                wait_vm<kDmaPerOp>();  // slab kt + 1 (Q of slab kt + 2 may be in flight)
                 __syncthreads();
                 if (kt + 3 == KT) next_tile(qb);  // slab kt's Q buffer takes the next tile's slab 0
                 gp ^= 1;
@@ -728,7 +738,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             // the epilogue's stores may be in flight) and published.  The epilogue's
             // stores drain while the next tile runs.
             __syncthreads();
-            wait_vm<C::kDmaPerOp>();
+            wait_vm<kDmaPerOp>();
             __syncthreads();
             gp ^= 1;
             gq = next3(gq);
