@@ -525,8 +525,8 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the owner-side step is one GPU's share of the work and this "
-              "build runs no collectives; run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the owner-side step is one GPU's share of the work and the "
+              "library runs no collectives; run it with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
