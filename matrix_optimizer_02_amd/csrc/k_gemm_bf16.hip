@@ -49,17 +49,6 @@
 #ifndef DMUON_BANDED
 #define DMUON_BANDED 1
 #endif
-#ifndef DMUON_SPREAD
-#define DMUON_SPREAD 1
-#endif
-// ends of the first and second load pieces, in eighths of a slab's loads
-// (-1: the tile configuration's own split)
-#ifndef DMUON_PIECE1
-#define DMUON_PIECE1 -1
-#endif
-#ifndef DMUON_PIECE2
-#define DMUON_PIECE2 -1
-#endif
 
 namespace dmuon {
 namespace {
@@ -84,11 +73,6 @@ struct TileCfg {
     static constexpr int WC = NW / 2;              // waves across the tile's columns (2 down its rows)
     static constexpr int RW = T / 2, CW = T / WC;  // rows, columns of one wave's sub-tile
     static constexpr int FI = RW / 32, FJ = CW / 32;  // MFMA blocks per wave per dim
-    // A slab's loads in pieces ending at these eighths (measured: with two
-    // waves per SIMD, half right after the barrier and half in the first
-    // k-step; with one, 3/8, 3/8 and 2/8 over the barrier and two k-steps).
-    static constexpr int kPiece1Eighths = DMUON_PIECE1 >= 0 ? DMUON_PIECE1 : (NW == 8 ? 4 : 3);
-    static constexpr int kPiece2Eighths = DMUON_PIECE2 >= 0 ? DMUON_PIECE2 : (NW == 8 ? 8 : 6);
     static constexpr int kOperandBytes = T * kRowBytes;
     static constexpr int kStageBytes = 2 * kOperandBytes;
     // B X: the P slab is kBK rows (k) of T long-side values
