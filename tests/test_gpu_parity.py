@@ -255,6 +255,32 @@ def test_mixed_precision_batch():
 
 # ---- degenerate cases, invariances, determinism --------------------------------------
 
+
+def test_repeated_steps_are_bit_identical():
+    """Tiles reach workgroups through per-XCD queues, so which workgroup
+    computes which tile changes from run to run, but every output element is
+    accumulated by one wave in one k order: three steps on the same inputs agree
+    bit for bit.  The set groups a Gram-space bucket (wide and tall matrices)
+    and two short-side ones: 666 tiles in a Gram or square launch and over
+    2000 in a B X launch, several for every CU."""
+    shapes = [(2048, 6144)] * 8 + [(2048, 2048)] * 8 + [(512, 1536)] * 6 + [(6144, 2048)] * 2
+    w = custom_workload("repeat", shapes, "bf16", "bf16")
+    G, M, W = make_inputs(w, "cuda", seed=11)
+    plan = d.plan_for(G, [x.dtype for x in W])
+    assert d.ALGO_GRAM_SPACE in [plan.bucket(b).algo for b in range(plan.info()[1])]
+    ws = d.workspace_for(plan)
+    runs = []
+    for rep in range(3):
+        say(f"case repeated step {rep}")
+        Mr, Wr = [x.clone() for x in M], [x.clone() for x in W]
+        d.muon_step_batched(plan, G, Mr, Wr, lr=LR, beta=BETA, eps=EPS, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((Mr, Wr))
+    for rep in (1, 2):
+        for i in range(len(shapes)):
+            assert torch.equal(runs[rep][0][i], runs[0][0][i]), (rep, shapes[i])
+            assert torch.equal(runs[rep][1][i].view(torch.int16), runs[0][1][i].view(torch.int16)), (rep, shapes[i])
+
 def test_zero_gradient_and_momentum():
     shapes = [(256, 512), (512, 128), (77, 77)]
     G = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
