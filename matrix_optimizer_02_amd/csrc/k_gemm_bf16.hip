@@ -155,9 +155,9 @@ struct LoadPlan {
 // workgroup overlap: the last two slabs of a tile load the next tile's first
 // P slab and first two Q slabs, and the epilogue stages the output through
 // the buffers of the tile's last slab, so the next tile's loads are in flight
-// while the output is written, and its stores drain while the next tile
-// runs.  Every output element is still accumulated by one wave in one k
-// order, so results do not depend on which workgroup takes which tile.
+// while the output is written.  Every output element is still accumulated by
+// one wave in one k order, so results do not depend on which workgroup takes
+// which tile.
 template <int T, int PHASE, bool FOLD>
 __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
@@ -716,11 +716,19 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             DMUON_SQ_FOLD(KT - 1, KS - 1, (KS - 1) & 1);
             __syncthreads();           // every wave is done with the last slab's buffers
             epilogue(cur, EBuf{pbuf(gp), qbuf(gq)});
+            // The queue ticket stays live through the epilogue.  Otherwise the
+            // compiler reuses its register there and, counting none of the direct
+            // loads, first waits for every load in flight (the next tile's first
+            // slabs included); its wait for the ticket falls here instead, where
+            // the tile-start wait below waits as long.
+            asm volatile("" ::"v"(taken));
             if (!has_next) break;
             // The next tile: P of its slab 0 and Q of its slabs 0 and 1 were issued
-            // in this tile's last two slabs; slab 0 is waited for (Q of slab 1 and
-            // the epilogue's stores may be in flight) and published.  The epilogue's
-            // stores drain while the next tile runs.
+            // in this tile's last two slabs, the epilogue's stores after them.
+            // Slab 0 is waited for and published; vector memory operations
+            // complete in issue order, stores included, so this also waits for
+            // all but the last kDmaPerOp stores (leaving more of them in flight
+            // measured no faster).
             __syncthreads();
             wait_vm<kDmaPerOp>();
             __syncthreads();
