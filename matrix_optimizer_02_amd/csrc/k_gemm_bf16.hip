@@ -46,9 +46,6 @@
 
 #include <cmath>
 
-#ifndef DMUON_BANDED
-#define DMUON_BANDED 1
-#endif
 
 namespace dmuon {
 namespace {
@@ -185,26 +182,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
         const GemmSeg& sg = args.seg[ti.s];
         ti.slot = local / sg.tiles_per_mat;
         const int t = local - ti.slot * sg.tiles_per_mat;
-        if (PHASE == kBX) {
-            if (DMUON_BANDED) {
-                bx_decode_banded(t, sg.tn, sg.tm, ti.I, ti.J);  // I: long-side tile, J: short-side tile
-            } else {
-                ti.I = t / sg.tm;
-                ti.J = t - ti.I * sg.tm;
-            }
-        } else {
-            if (DMUON_BANDED) {
-                tri_decode_banded(t, sg.tm, ti.I, ti.J);
-            } else {
-                int tt = t, i = 0;
-                while (tt >= sg.tm - i) {
-                    tt -= sg.tm - i;
-                    ++i;
-                }
-                ti.I = i;
-                ti.J = i + tt;
-            }
-        }
+        if (PHASE == kBX)
+            bx_decode_banded(t, sg.tn, sg.tm, ti.I, ti.J);  // I: long-side tile, J: short-side tile
+        else
+            tri_decode_banded(t, sg.tm, ti.I, ti.J);
     };
     // The P operand (B X: X, read k-major) of a tile's matrix, and the leading
     // dimension of the K-contiguous rows (Q's, and P's outside B X): the K extent.

@@ -25,11 +25,6 @@
 #include "kcommon.h"
 #include "launch.h"
 
-#ifndef DMUON_RES_UNROLL
-#define DMUON_RES_UNROLL 1
-#endif
-#define DMUON_PRAGMA_(x) _Pragma(#x)
-#define DMUON_PRAGMA(x) DMUON_PRAGMA_(x)
 
 namespace dmuon {
 namespace {
@@ -82,7 +77,7 @@ __device__ __forceinline__ void sym_product(const char* P, int row_bytes, int K,
     bf16x8 fa = ld8(P, loff(ra, 8 * khalf, row_bytes));
     bf16x8 fb0 = ld8(P, loff(rb0, 8 * khalf, row_bytes));
     bf16x8 fb1 = ld8(P, loff(rb0 + 32, 8 * khalf, row_bytes));
-    DMUON_PRAGMA(unroll DMUON_RES_UNROLL)
+    #pragma unroll 1
     for (int k = 16; k < K; k += 16) {
         const int c = k + 8 * khalf;
         const bf16x8 na = ld8(P, loff(ra, c, row_bytes));
