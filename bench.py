@@ -22,8 +22,10 @@ the Gram space runs).
 ``roofline`` covers the dominant kernel, the B X product, timed live with HIP
 events at its launch boundaries inside the timed steps.
 ``elementwise`` gives the bandwidth-bound passes of the same steps (prep:
-momentum, cast and norm partials; apply: the update) in GB/s of their required
-traffic against the 8 TB/s HBM peak.  ``adamw`` times the AdamW companion
+momentum, cast and norm partials; apply: the update of the matrices that the
+last B X launch does not update from its epilogue -- on the bf16 owner shares,
+none) in GB/s of their required traffic against the 8 TB/s HBM peak;
+``update_in_last_bx`` counts the updates written by that epilogue.  ``adamw`` times the AdamW companion
 step on Llama-3.1-8B's non-Muon parameters (one GPU's 1/8 element share) the
 same way.  ``graph`` replays the same step from a HIP graph (no host enqueueing
 in the timed span; the number that matters for small, launch-bound
@@ -99,24 +101,42 @@ def executed_flops(m: int, n: int, seg_len: int, steps: int = NS_STEPS, resident
     return out
 
 
-def dominant_kernel(seg_len, resident, bx_flops_grouped, res_flops, bx_ms_per_step, gram0_ms, f32_only,
-                    steps: int = NS_STEPS):
-    """(kernel name, average launch ms, flops per launch) of the kernel the
-    roofline covers.  With any bucket in the grouped launches it is the B X
-    product: the B X phases that launch anything are the iterations that close
-    a segment of such a bucket (every iteration on the short side), each one
-    grouped launch per tile class.  With every bucket resident it is the
-    resident kernel, one launch per step, timed inside iteration 0's Gram
-    phase.  bx_ms_per_step holds each timed step's B X phase times."""
-    grouped_len = {L for L, res in zip(seg_len, resident) if not res}
-    if grouped_len:
-        bx_iters = [k for k in range(steps) if any(k % L == L - 1 or k == steps - 1 for L in grouped_len)]
-        bx_ms = [row[k] for row in bx_ms_per_step for k in bx_iters]
+def bx_flops_by_iteration(w, seg_len, resident, steps: int = NS_STEPS):
+    """B X flops of each iteration's grouped launch: a matrix's closing product
+    runs in the iterations that end one of its segments (every iteration on
+    the short side; the last segment may be shorter)."""
+    out = [0] * steps
+    for s, L, res in zip(w.matrices, seg_len, resident):
+        if res:
+            continue
+        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
+        for k in range(steps):
+            if k % L == L - 1 or k == steps - 1:
+                out[k] += bx_flops(m, n)
+    return out
+
+
+def dominant_kernel(bx_by_iter, any_fused, res_flops, bx_ms_per_step, gram0_ms, f32_only, steps: int = NS_STEPS):
+    """(kernel name, average launch ms, flops per launch, iterations timed) of
+    the kernel the roofline covers.  With any bucket in the grouped launches it
+    is the B X product: its launches are the iterations that close a segment of
+    such a bucket, one grouped launch per tile class.  When the last of them
+    also writes parameter updates (any_fused) it is an instance of its own,
+    timed apart, and the roofline covers the plain ones (unless it is the only
+    one).  With every bucket resident it is the resident kernel, one launch per
+    step, timed inside iteration 0's Gram phase.  bx_ms_per_step holds each
+    timed step's B X phase times."""
+    bx_iters = [k for k in range(steps) if bx_by_iter[k] > 0]
+    if bx_iters:
+        plain = [k for k in bx_iters if not (any_fused and k == steps - 1)] or bx_iters
+        bx_ms = [row[k] for row in bx_ms_per_step for k in plain]
         kernel = ("ns_gemm_f32_kernel<BX> (X' = s (a X + B X), fp32 MFMA)" if f32_only
-                  else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)")
-        return kernel, sum(bx_ms) / len(bx_ms), bx_flops_grouped / len(bx_iters)
+                  else "ns_gemm_bf16_kernel<256, BX> (X' = s B' X, B' = aI + B)" + (
+                      "; the plain launches (the last one, writing the updates, is timed apart)"
+                      if any_fused and len(plain) < len(bx_iters) else ""))
+        return kernel, sum(bx_ms) / len(bx_ms), sum(bx_by_iter[k] for k in plain) / len(plain), plain
     return ("ns_resident_kernel (every iteration of a small bf16 bucket in one launch, the matrix in LDS)",
-            gram0_ms, res_flops)
+            gram0_ms, res_flops, [])
 
 
 def read_traffic(kernel_tag: str):
@@ -611,6 +631,8 @@ def main(argv=None):
     seg_len = [plan.bucket(plan.query(i).bucket).gram_restart for i in range(w.count)]
     gram_space = [plan.bucket(plan.query(i).bucket).algo == d.ALGO_GRAM_SPACE for i in range(w.count)]
     resident = [plan.bucket(plan.query(i).bucket).resident for i in range(w.count)]
+    # matrices whose update the last B X launch writes (the apply pass skips them)
+    fused = [plan.update_fused(i, NS_STEPS) for i in range(w.count)]
     alg = dense = 0
     execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}  # grouped launches
     res_flops = 0  # the resident kernel's (every iteration of a small bucket in one launch)
@@ -630,9 +652,11 @@ def main(argv=None):
     peak = FP32_PEAK_TFLOPS if f32_only else BF16_PEAK_TFLOPS
     phase_tot = {k: sum(p[j] for p in per for j, nm in enumerate(names) if kind_of(nm) == k) / len(per)
                  for k in execd}
-    kernel, launch_ms, flops_per_launch = dominant_kernel(
-        seg_len, resident, execd["bx"], res_flops, [[p[names.index(f"bx{k}")] for k in range(NS_STEPS)] for p in per],
-        avg["gram0"], f32_only)
+    bx_by_iter = bx_flops_by_iteration(w, seg_len, resident)
+    assert sum(bx_by_iter) == execd["bx"]
+    bx_rows = [[p[names.index(f"bx{k}")] for k in range(NS_STEPS)] for p in per]
+    kernel, launch_ms, flops_per_launch, bx_plain = dominant_kernel(
+        bx_by_iter, any(fused), res_flops, bx_rows, avg["gram0"], f32_only)
     achieved = flops_per_launch / (launch_ms / 1e3) / 1e12
     traffic = (read_traffic("bx_gemm_bf16_llama8b")
                if args.workload == "llama3.1-8b_owner_1of8" and not args.tuning_cache else None)
@@ -676,22 +700,43 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "launch_ms": round(launch_ms, 4), "flops_per_launch": flops_per_launch},
+                     "launch_ms": round(launch_ms, 4), "flops_per_launch": flops_per_launch,
+                     "iterations": bx_plain},
     }
     # the bandwidth-bound passes of the same steps, against the HBM roofline
     elems = w.elements()
     gsz = 2 if paths == {"bf16"} else 4
     psz = 2 if all(s.param_dtype == "bf16" for s in w.matrices) else 4
     prep_bytes = elems * (gsz + 4 + 4 + gsz)   # read G, M; write M', U (as X)
-    apply_bytes = elems * (gsz + psz + psz)     # read O (X), W; write W'
+    # the apply pass: read O (X), W; write W' -- for the matrices the last B X does not update
+    psize = lambda s: 2 if s.param_dtype == "bf16" else 4
+    apply_bytes = sum(s.rows * s.cols * (gsz + 2 * psize(s)) for s, f in zip(w.matrices, fused) if not f)
+    fused_elems = sum(s.rows * s.cols for s, f in zip(w.matrices, fused) if f)
+
+    def rate(nbytes, ms):
+        if nbytes == 0 or ms <= 0:
+            return {"gbps": None, "frac_hbm": None}
+        return {"gbps": round(nbytes / (ms / 1e3) / 1e9, 1), "frac_hbm": round(nbytes / (ms / 1e3) / HBM_PEAK_BPS, 4)}
+
     out["elementwise"] = {
-        "prep": {"bytes": prep_bytes, "ms": round(avg["prep"], 4),
-                 "gbps": round(prep_bytes / (avg["prep"] / 1e3) / 1e9, 1),
-                 "frac_hbm": round(prep_bytes / (avg["prep"] / 1e3) / HBM_PEAK_BPS, 4)},
-        "apply": {"bytes": apply_bytes, "ms": round(avg["apply"], 4),
-                  "gbps": round(apply_bytes / (avg["apply"] / 1e3) / 1e9, 1),
-                  "frac_hbm": round(apply_bytes / (avg["apply"] / 1e3) / HBM_PEAK_BPS, 4)},
+        "prep": {"bytes": prep_bytes, "ms": round(avg["prep"], 4), **rate(prep_bytes, avg["prep"])},
+        "apply": {"bytes": apply_bytes, "ms": round(avg["apply"], 4), **rate(apply_bytes, avg["apply"]),
+                  "matrices": w.count - sum(fused)},
+        "update_in_last_bx": {"matrices": sum(fused), "elements": fused_elems,
+                              "bytes": fused_elems * 4,
+                              "note": "read W, write W' (bf16) from the last B X launch's epilogue; "
+                                      "the final X never goes to HBM, so the apply pass's 6 bytes "
+                                      "per element become 4, inside that launch"},
     }
+    last = NS_STEPS - 1
+    if any(fused) and bx_by_iter[last] > 0 and last not in bx_plain:
+        last_ms = sum(r[last] for r in bx_rows) / len(bx_rows)
+        out["bx_update_launch"] = {
+            "kernel": "ns_gemm_bf16_kernel<256, BX, fused update>: the last iteration's B X, whose epilogue "
+                      "writes W' for the matrices it updates",
+            "ms": round(last_ms, 4), "flops": bx_by_iter[last],
+            "tflops": round(bx_by_iter[last] / (last_ms / 1e3) / 1e12, 1),
+            "update_bytes": fused_elems * 4, "matrices": sum(fused)}
     out["graph"] = graph_bench(d, plan, G, M, W, ws, max(args.steps, 50 if ms_per_step < 5 else 0), w.count)
     if tuning_info is not None:
         out["tuning"] = tuning_info
@@ -716,8 +761,9 @@ def main(argv=None):
         out["roofline"]["frac_of_sustained_mfma"] = (round(achieved / ce["mfma_bf16"]["tflops"], 4)
                                                      if not f32_only else None)
         for k in ("prep", "apply"):
-            out["elementwise"][k]["frac_of_copy"] = round(out["elementwise"][k]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
-            out["elementwise"][k]["frac_of_mix"] = round(out["elementwise"][k]["gbps"] / (ce["mix"][k]["tbps"] * 1e3), 4)
+            gb = out["elementwise"][k]["gbps"]
+            out["elementwise"][k]["frac_of_copy"] = round(gb / (ce["copy"]["tbps"] * 1e3), 4) if gb else None
+            out["elementwise"][k]["frac_of_mix"] = round(gb / (ce["mix"][k]["tbps"] * 1e3), 4) if gb else None
         if "adamw" in out:
             out["adamw"]["frac_of_copy"] = round(out["adamw"]["gbps"] / (ce["copy"]["tbps"] * 1e3), 4)
             out["adamw"]["frac_of_mix"] = round(out["adamw"]["gbps"] / (ce["mix"]["adamw"]["tbps"] * 1e3), 4)

@@ -143,7 +143,12 @@ typedef struct {
     uint32_t xcd_remap;      /* bf16 path: bit per phase (1 Gram, 2 square, 4 B X, 8 prod) whose launch
                                 gives each XCD a contiguous run of the bucket's tiles (neighbouring tiles
                                 share operand panels in that XCD's L2); DMUON_XCD_REMAP_DEFAULT: B X only */
-    int32_t reserved;        /* 0 */
+    int32_t apply_pass;      /* 0 (default): on the bf16 path, the last B X launch writes the update
+                                (or the output) of every member with a bf16 parameter (output) and
+                                cols a multiple of 8 from its epilogue, and X is never written back;
+                                1: a separate elementwise pass writes it from the final X for every
+                                member, as it does for the other members.  The two give identical
+                                bits; other values are INVALID_ARG */
     double cost_ms_per_matrix; /* measured time of one matrix's Newton-Schulz iterations; when every
                                   bucket of a plan has one > 0, buckets are ordered by count times it
                                   instead of the dense cost */
@@ -244,6 +249,21 @@ DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t buc
  * be latency-bound.  Same arithmetic and roundings either way. */
 DMUON_API dmuon_status muon_plan_bucket_resident(const dmuon_plan* plan, int32_t bucket, int32_t* resident);
 
+/* Where a step (or orthogonalisation) with ns_steps iterations writes matrix
+ * idx's update (output): 1 from the epilogue of its last B X launch, which
+ * then never writes the final X back, 0 in the separate elementwise pass.
+ * The owner applies the update right after the matrix's Newton-Schulz
+ * iteration (DMuon abstract; DMuon explainer on gist.science, section 2.1
+ * Owner-Centric Executiestrategie); written by the product that ends the
+ * iteration, the orthogonalised matrix makes no round trip through memory.
+ * The epilogue takes a bf16 parameter (output) with cols a multiple of 8
+ * whose bucket runs tiled bf16 launches (not resident) and whose
+ * configuration has apply_pass 0, when ns_steps > 0; the two routes give
+ * identical bits.  Host only.  Errors: INVALID_ARG (null plan or fused, idx
+ * out of range, ns_steps < 0). */
+DMUON_API dmuon_status muon_plan_update_fused(const dmuon_plan* plan, int32_t idx, int32_t ns_steps,
+                                              int32_t* fused);
+
 /* The configuration a bucket runs with, as a tuning entry (key, tile, algo,
  * restart, remap bits; cost_ms_per_matrix as given to the plan, else 0). */
 DMUON_API dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t bucket, dmuon_tune_entry* out);
@@ -287,7 +307,9 @@ DMUON_API void muon_plan_destroy(dmuon_plan* plan);
  * place in momenta[i], fp32), normalisation, ns_steps NS iterations on the
  * short side (or in the Gram space, per bucket: dmuon_algo), and the
  * in-place parameter update of params[i] (param_dtype; bf16 results are
- * rounded to nearest even once, from fp32).
+ * rounded to nearest even once, from fp32), written by the last B X
+ * launch's epilogue where muon_plan_update_fused says so, else by an
+ * elementwise pass.
  *   grads[i]   device, rows x cols, grad_dtype, read only, must not alias
  *   momenta[i] device, rows x cols, fp32, read and written
  *   params[i]  device, rows x cols, param_dtype, read and written

@@ -2,8 +2,9 @@
 // the per-call matrix table, and the launch sequence of one step
 //   records -> prep (momentum, U, X, norm partials) -> norms
 //   -> ns_steps x (Gram, square, prod, BX), each phase a grouped launch per
-//      tile class (prod: two, for the Gram-space buckets)
-//   -> apply (update or output).
+//      tile class (prod: two, for the Gram-space buckets); the last BX writes
+//      the update (or output) of the bf16 matrices it can from its epilogue
+//   -> apply (update or output) of the others.
 // No device memory is allocated and nothing is synchronised: everything is
 // enqueued on the caller's stream.
 #include <algorithm>
@@ -114,11 +115,12 @@ struct SegSpec {
     const BucketPlan* bp;
     int64_t p_off, q_off, o_off;
     int32_t first_iter;
+    int32_t fuse = 0;  // B X closing the last segment (the epilogue writes the fused matrices' dst)
 };
 
 // One grouped launch per tile class over the given products of one phase.
-hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const StepParams& sp, int phase,
-                       const std::vector<SegSpec>& segs, hipStream_t stream) {
+hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const DevMatRec* recs,
+                       const StepParams& sp, int phase, const std::vector<SegSpec>& segs, hipStream_t stream) {
     for (const TileClass& tc : kClasses) {
         GemmArgs ga{};
         ga.ws = ws;
@@ -127,6 +129,10 @@ hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const Step
         ga.a = sp.a;
         ga.b = sp.b;
         ga.c = sp.c;
+        ga.recs = recs;
+        ga.lr = sp.lr;
+        ga.wd = sp.wd;
+        ga.update = sp.update;
         ga.phase = phase;
         auto flush = [&]() -> hipError_t {
             if (ga.nseg == 0) return hipSuccess;
@@ -155,6 +161,7 @@ hipError_t launch_segs(char* ws, uint32_t* queue, const float* scale, const Step
             s.plan_base = bp.plan_base;
             s.first_iter = ss.first_iter;
             s.xcd_remap = (int32_t)((bp.xcd_mask >> phase) & 1u);
+            s.fuse = phase == kBX && bp.path == kPathBF16 ? ss.fuse : 0;
             s.first_block = ga.total_blocks;
             s.m_pad = bp.m_pad;
             s.n_pad = bp.n_pad;
@@ -264,8 +271,10 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         r.partial_off = mp.partial_off;
         r.prep_begin = prep_blocks;
         prep_blocks += prep_blocks_of(mp.r_pad, mp.c_pad);
+        // the last B X launch writes this update, or the apply pass does
+        r.fused = update_fused(bp, mp, steps);
         r.apply_begin = apply_blocks;
-        apply_blocks += apply_blocks_of(mp.rows, mp.cols);
+        if (!r.fused) apply_blocks += apply_blocks_of(mp.rows, mp.cols);
         r.rows = (int32_t)mp.rows;
         r.cols = (int32_t)mp.cols;
         r.r_pad = (int32_t)mp.r_pad;
@@ -322,7 +331,7 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         return (int64_t)(copy == 0 ? p->buckets[b].off_x0 : p->buckets[b].off_x1);
     };
     auto phase_done = [&](int phase) -> bool {
-        const bool ok = launch_segs(ws, queue, scale, sp, phase, segs, stream) == hipSuccess;
+        const bool ok = launch_segs(ws, queue, scale, table, sp, phase, segs, stream) == hipSuccess;
         segs.clear();
         return ok;
     };
@@ -355,7 +364,8 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
         for (size_t b = 0; b < nb; ++b) {
             if (resident[b] || j[b] != lc[b] - 1) continue;
             const int64_t pfin = j[b] == 0 ? roles[b].q : roles[b].p2;  // P_Lc
-            segs.push_back({&p->buckets[b], xoff(b, xcur[b]), pfin, xoff(b, 1 - xcur[b]), it == j[b] ? 1 : 0});
+            segs.push_back({&p->buckets[b], xoff(b, xcur[b]), pfin, xoff(b, 1 - xcur[b]), it == j[b] ? 1 : 0,
+                            it == steps - 1 ? 1 : 0});
         }
         if (!phase_done(kBX) || !mark()) return DMUON_ERR_HIP;
 

@@ -101,6 +101,7 @@ struct BucketPlan {
     int32_t seg_len;       // iterations per segment: 1 (short side) or the Gram-space restart interval
     uint32_t xcd_mask;     // bf16: phases (bit per Phase) whose launch deals each XCD a contiguous tile run
     double cost_ms;        // measured per-matrix cost from a tuned entry, 0 if none
+    int32_t apply_pass;    // 1: the update is written by the elementwise pass, never by B X
     int32_t tile;          // tile granularity g
     int64_t m_pad, n_pad;
     std::vector<int32_t> members;  // input indices, slot order
@@ -149,7 +150,19 @@ struct DevMatRec {
     int32_t src_dtype, dst_dtype, path;
     float upd_scale;       // sqrt(max(1, rows / cols))
     int32_t final_copy;    // X copy (0 | 1) that holds the orthogonalised matrix
+    int32_t fused;         // 1: the last B X launch writes dst (update or output) from its
+                           // epilogue; X is not written back and the apply pass skips it
 };
+
+// Whether a step with `steps` iterations writes matrix mp's update from the
+// epilogue of its last B X launch (else the apply pass writes it): a bf16
+// parameter with cols a multiple of 8 (16-byte chunks of whole rows), in a bf16
+// bucket of tiled launches (not resident) that keeps the default route.
+inline bool update_fused(const BucketPlan& bp, const MatPlan& mp, int32_t steps) {
+    const bool resident = bp.algo == DMUON_ALGO_SHORT_SIDE && resident_shape(bp.path, bp.m_pad, bp.n_pad);
+    return steps > 0 && bp.path == kPathBF16 && !resident && bp.apply_pass == 0 &&
+           mp.param_dtype == DMUON_BF16 && mp.cols % 8 == 0;
+}
 
 // Apply kernel: each block covers kApplyElems elements of the real matrix.
 constexpr int kApplyThreads = 256;

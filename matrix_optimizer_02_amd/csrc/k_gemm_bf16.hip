@@ -2,7 +2,9 @@
 // phase over every bucket of the batch:
 //   Gram    A  = s X X^T           upper-triangle tiles only, mirrored store
 //   square  B' = a I + b A + c A A^T   (A A = A A^T: A is symmetric) upper tiles only
-//   BX      X' = s B' X            into the other X copy
+//   BX      X' = s B' X            into the other X copy; in the last
+//                                  iteration (FUSED instance) the epilogue
+//                                  writes the parameter update W' instead
 //   prod    C  = P Q               P, Q symmetric and commuting (the Gram-space
 //                                  recurrence's products), upper tiles only
 // X' = a X + B X is computed as (a I + B) X: the a X term rides on B's
@@ -154,8 +156,10 @@ struct LoadPlan {
 // the buffers of the tile's last slab, so the next tile's loads are in flight
 // while the output is written.  Every output element is still accumulated by
 // one wave in one k order, so results do not depend on which workgroup takes
-// which tile.
-template <int T, int PHASE, bool FOLD>
+// which tile.  FUSED selects the square's variant with b A folded into its
+// accumulators, and B X's variant whose epilogue can write parameter updates
+// (the last iteration's launch); the other phases ignore it.
+template <int T, int PHASE, bool FUSED>
 __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArgs args) {
     using C = TileCfg<T>;
     // P buffers 0, 1, then Q buffers 0, 1, 2, kOperandBytes each
@@ -295,10 +299,10 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
     // (A is symmetric); one more MFMA per fragment against (b / c) times the
     // identity (rows k' of the tile) adds (b / c) A[I T + r][J T + c] to
     // acc[r][c].  b / c goes in as two bf16 parts, so it keeps about 16 bits.
-    // FOLD (the launch takes it when c != 0 and |b / c| <= 64; the quintic's
+    // FUSED (the launch takes it when c != 0 and |b / c| <= 64; the quintic's
     // b / c is -2.35): for other coefficients the epilogue reads A's block back
     // instead, in a kernel of its own.
-    constexpr bool sq_fold = PHASE == kSquare && FOLD;
+    constexpr bool sq_fold = PHASE == kSquare && FUSED;
     const float sq_bc = sq_fold ? args.b / args.c : 0.f;
     const __bf16 sq_hi = (__bf16)sq_bc;
     const __bf16 sq_lo = (__bf16)(sq_bc - (float)sq_hi);
@@ -482,6 +486,122 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             *reinterpret_cast<shortx8*>(dst + (int64_t)(r0 + i16) * ld + cb) = v;
         }
     };
+    // The parameter update written by the last B X launch (FUSED), for a bf16
+    // parameter: per element W' = keep W + coef O (or, for the output of an
+    // orthogonalisation, W' = O), O being the bf16 value X' would get and
+    // keep, coef the apply pass's own factors, so the result is the apply
+    // pass's bit for bit.  Waves 0 .. 3 (kUpdWaves) do the update: they hold
+    // the accumulators of piece 0 of E, and load parameter chunks into
+    // registers only once those are staged, so the accumulators of piece 1
+    // (waves 4 .. 7) and the parameter chunks are never live together.
+    //   piece 0: waves 0 .. 3 stage it; barrier; they load W's chunks of piece
+    //            0, update and store them, then load those of piece 1
+    //   piece 1: barrier (E free); waves 4 .. 7 stage it; barrier; waves 0 .. 3
+    //            update and store it
+    // (T = 128: one piece, all four waves.)  Each worker lane takes kUpd
+    // 16-byte chunks (8 bf16) of a piece: along parameter rows for a wide or
+    // square matrix (W[c][r]: E's rows, as store_rows), along E's columns for a
+    // tall one (W[r][c]: through the transposing read, as store_cols).
+    constexpr int kUpdWaves = 4;
+    static_assert(C::kEHalves == 1 ? C::NW == kUpdWaves : (C::kEHalves == 2 && C::NW == 2 * kUpdWaves),
+                  "the update waves hold piece 0");
+    constexpr int kUpd = kERows * C::kEChunks / (64 * kUpdWaves);
+    static_assert((T / 16) * (kERows / 32) / kUpdWaves == kUpd, "both layouts take kUpd chunks a lane");
+    auto update_epilogue = [&](const TileInfo& ti, const EBuf& ebuf, const auto* rec, auto&& stage, int etid) {
+        const int64_t rows = rec->rows, cols = rec->cols;
+        const bool tall = rec->transposed != 0;
+        uint16_t* const W = static_cast<uint16_t*>(rec->dst);  // bf16 (fused records only)
+        const float coef = -args.lr * rec->upd_scale;
+        const float keep = 1.0f - args.lr * args.wd;
+        const int ut = etid & (64 * kUpdWaves - 1);  // lane among the update waves
+        const int g = (ut & 63) >> 4, i16 = ut & 15, k4 = i16 >> 2, q4 = i16 & 3, uw = ut >> 6;
+        constexpr int kRowBlocks = T / 16;
+        // chunk u of piece h: the parameter row and column it covers (cols a
+        // multiple of 8: a chunk is inside the matrix or wholly outside),
+        // and where its O values sit in E
+        auto chunk = [&](int h, int u, int64_t& prow, int64_t& pcol, int& erow_, int& ecol) {
+            const int c0 = ti.J * T + h * kERows, r0 = ti.I * T;
+            if (!tall) {  // W[c][r]: E row = c, chunk along r
+                const int qq = ut + 64 * kUpdWaves * u;
+                erow_ = qq / C::kEChunks;
+                ecol = 8 * (qq % C::kEChunks);
+                prow = c0 + erow_;
+                pcol = r0 + ecol;
+            } else {  // W[r][c]: 8 consecutive c of one r
+                const int wv = kUpdWaves * u + uw;
+                const int rr = (wv % kRowBlocks) * 16, cb = (wv / kRowBlocks) * 32 + 8 * g;
+                erow_ = cb;
+                ecol = rr;
+                prow = r0 + rr + i16;
+                pcol = c0 + cb;
+            }
+        };
+        auto inside = [&](int64_t prow, int64_t pcol) { return prow < rows && pcol < cols; };
+        u32x4_t w[kUpd];
+        auto load_w = [&](int h) {
+            if (!args.update) return;
+            #pragma unroll
+            for (int u = 0; u < kUpd; ++u) {
+                int64_t prow, pcol;
+                int er, ec;
+                chunk(h, u, prow, pcol, er, ec);
+                if (inside(prow, pcol)) w[u] = ld_stream<u32x4_t>(W + prow * cols + pcol);
+            }
+        };
+        auto update = [&](int h) {
+            #pragma unroll
+            for (int u = 0; u < kUpd; ++u) {
+                int64_t prow, pcol;
+                int er, ec;
+                chunk(h, u, prow, pcol, er, ec);
+                u32x4_t o;
+                if (!tall) {
+                    o = *reinterpret_cast<const u32x4_t*>(erow(ebuf, er) + (((ec >> 3) ^ swizzle_e<T>(er)) << 4));
+                } else {
+                    // every lane takes part in the transposing reads: the empty
+                    // asm keeps them out of the branch below
+                    shortx4 hv[2];
+                    #pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_shortx4*)((__attribute__((address_space(3))) char*)e_ptr(ebuf, er + 4 * hh + k4, ec + 4 * q4)));
+                    o = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    asm volatile("" : "+v"(o));
+                }
+                if (inside(prow, pcol)) {
+                    if (args.update) {
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t ov = o[e], wv = w[u][e];
+                            const float lo = fmaf(coef, __uint_as_float(ov << 16), keep * __uint_as_float(wv << 16));
+                            const float hi = fmaf(coef, __uint_as_float(ov & 0xffff0000u),
+                                                  keep * __uint_as_float(wv & 0xffff0000u));
+                            o[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                        }
+                    }
+                    st_stream<u32x4_t>(W + prow * cols + pcol, o);
+                }
+            }
+        };
+        if constexpr (C::kEHalves == 1) {
+            stage(0);
+            __syncthreads();
+            load_w(0);
+            update(0);
+        } else {
+            if (my_piece == 0) stage(0);
+            __syncthreads();
+            if (wave < kUpdWaves) {
+                load_w(0);
+                update(0);
+                load_w(1);
+            }
+            __syncthreads();  // E is free again
+            if (my_piece == 1) stage(1);
+            __syncthreads();
+            if (wave < kUpdWaves) update(1);
+        }
+    };
     auto epilogue = [&](const TileInfo& ti, const EBuf& ebuf) {
         // Lane indices passed through an empty asm statement: the epilogue's
         // per-lane addresses are then computed here, once per tile, rather
@@ -504,9 +624,15 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             const int64_t ldn = sg.n_pad;
             uint16_t* Xd = reinterpret_cast<uint16_t*>(args.ws + sg.o_off + ti.slot * sg.x_stride) +
                            (int64_t)ti.J * T * ldn + (int64_t)ti.I * T;
-            #pragma unroll
-            for (int h = 0; h < C::kEHalves; ++h) {
-                if (my_piece == h) {
+            bool fused = false;
+            if constexpr (FUSED) {
+                // the last segment's closing product of a matrix whose record
+                // says fused: the epilogue writes its update instead of X'
+                typedef const __attribute__((address_space(4))) DevMatRec crec_t;
+                const crec_t* rec = reinterpret_cast<const crec_t*>(reinterpret_cast<uintptr_t>(args.recs + plan_idx));
+                fused = sg.fuse != 0 && rec->fused != 0;
+                // piece h of E from the accumulators of the waves holding its columns
+                auto stage = [&](int h) {
                     #pragma unroll
                     for (int i = 0; i < C::FI; ++i)
                         #pragma unroll
@@ -522,10 +648,35 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                                       ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 3]) << 16);
                                 *reinterpret_cast<uint2*>(e_ptr(ebuf, c, r0)) = o;
                             }
+                };
+                if (fused) update_epilogue(ti, ebuf, rec, stage, etid);
+            }
+            if (!fused) {
+                // (the same staging as the fused path's, written out: the
+                // lambda here changes this kernel's register allocation)
+                #pragma unroll
+                for (int h = 0; h < C::kEHalves; ++h) {
+                    if (my_piece == h) {
+                        #pragma unroll
+                        for (int i = 0; i < C::FI; ++i)
+                            #pragma unroll
+                            for (int j = 0; j < C::FJ; ++j)
+                                #pragma unroll
+                                for (int v4 = 0; v4 < 4; ++v4) {
+                                    const int r0 = wr * C::RW + i * 32 + 8 * v4 + 4 * ekhalf;
+                                    const int c = wc * C::CW + j * 32 + elrow - h * kERows;
+                                    uint2 o;
+                                    o.x = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 0]) |
+                                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 1]) << 16);
+                                    o.y = (uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 2]) |
+                                          ((uint32_t)f32_to_bf16(first_scale * acc[i][j][4 * v4 + 3]) << 16);
+                                    *reinterpret_cast<uint2*>(e_ptr(ebuf, c, r0)) = o;
+                                }
+                    }
+                    __syncthreads();
+                    store_rows(etid, ebuf, Xd + (int64_t)h * kERows * ldn, ldn);
+                    if (h + 1 < C::kEHalves) __syncthreads();  // before the next piece overwrites E
                 }
-                __syncthreads();
-                store_rows(etid, ebuf, Xd + (int64_t)h * kERows * ldn, ldn);
-                if (h + 1 < C::kEHalves) __syncthreads();  // before the next piece overwrites E
             }
         } else {
             // Out[I T + r][J T + c] = C[r][c] = E[c][r] and, off the diagonal, the
@@ -751,13 +902,19 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)persistent_grid<T>(a.total_blocks)), block(TileCfg<T>::NT);
     // the square folds its b A term into the accumulators when b / c is moderate
     const bool fold = a.c != 0.f && std::fabs(a.b / a.c) <= 64.f;
+    // B X writes parameter updates from its epilogue when a segment asks for it
+    bool fuse = false;
+    for (int i = 0; i < a.nseg; ++i) fuse = fuse || a.seg[i].fuse != 0;
     switch (a.phase) {
         case kGram: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kGram, true>), grid, block, 0, stream, a); break;
         case kSquare:
             if (fold) hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare, true>), grid, block, 0, stream, a);
             else hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kSquare, false>), grid, block, 0, stream, a);
             break;
-        case kBX: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX, true>), grid, block, 0, stream, a); break;
+        case kBX:
+            if (fuse) hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kBX, false>), grid, block, 0, stream, a);
+            break;
         case kProd: hipLaunchKernelGGL((ns_gemm_bf16_kernel<T, kProd, true>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }

@@ -76,6 +76,8 @@ struct GemmSeg {
     int32_t plan_base;      // plan index of slot 0
     int32_t first_iter;     // apply the normalisation scale s (Gram s^2, B X s)
     int32_t xcd_remap;      // bf16: each XCD takes a contiguous run of this segment's tiles
+    int32_t fuse;           // B X closing the last segment: for matrices whose record says
+                            // fused, the epilogue writes dst (update or output) instead of X'
     int64_t m_pad, n_pad;
     int64_t p_off, q_off, o_off;  // operand P, operand Q (kProd, kBX), output
     int64_t x_stride, a_stride;   // per-slot bytes
@@ -86,6 +88,9 @@ struct GemmArgs {
     uint32_t* queue;     // bf16: kQueueWords counters, zero at launch (kXcds tile counters, then the
                          // count of finished workgroups); the launch's last workgroup zeroes them again
     const float* scale;  // per plan index: 1 / (||U|| + eps)
+    const DevMatRec* recs;  // per plan index (read by B X segments with fuse set)
+    float lr, wd;           // the update W' = W (1 - lr wd) - lr s O of such segments ...
+    int32_t update;         // ... when 1; 0: dst = O
     float a, b, c;
     int32_t phase;
     int32_t nseg;

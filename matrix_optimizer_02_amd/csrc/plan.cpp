@@ -130,6 +130,7 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
             bp.seg_len = gram ? restart : 1;
             bp.xcd_mask = kDefaultXcdMask;
             bp.cost_ms = 0.0;
+            bp.apply_pass = 0;
             // a tuned entry for this shape overrides the defaults above
             const dmuon_tune_entry* e = nullptr;
             for (int32_t t = 0; t < ntuned && e == nullptr; ++t) {
@@ -143,7 +144,7 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
                 (e->algo != DMUON_ALGO_AUTO && e->algo != DMUON_ALGO_SHORT_SIDE && e->algo != DMUON_ALGO_GRAM_SPACE) ||
                 (e->algo == DMUON_ALGO_GRAM_SPACE && bp.path != kPathBF16) || e->gram_restart < 0 ||
                 (e->xcd_remap != DMUON_XCD_REMAP_DEFAULT && (e->xcd_remap & ~kAllPhasesMask) != 0) ||
-                e->reserved != 0 || !(e->cost_ms_per_matrix >= 0.0))
+                (e->apply_pass != 0 && e->apply_pass != 1) || !(e->cost_ms_per_matrix >= 0.0))
                 throw InvalidEntry();
             if (e->tile != 0) bp.tile = e->tile;
             // Entries are keyed by padded dims, so one measured on some shapes
@@ -159,6 +160,7 @@ extern "C" dmuon_status muon_plan_ex(const dmuon_matrix_desc* descs, int32_t cou
             if (bp.algo == DMUON_ALGO_GRAM_SPACE && e->gram_restart > 0) bp.seg_len = e->gram_restart;
             if (e->xcd_remap != DMUON_XCD_REMAP_DEFAULT) bp.xcd_mask = e->xcd_remap;
             bp.cost_ms = e->cost_ms_per_matrix;
+            bp.apply_pass = e->apply_pass;
         }
         // a bucket's launch must stay within 32-bit block ids (B X has the
         // most tiles per matrix)
@@ -304,6 +306,15 @@ extern "C" dmuon_status muon_plan_bucket_resident(const dmuon_plan* plan, int32_
     return DMUON_OK;
 }
 
+extern "C" dmuon_status muon_plan_update_fused(const dmuon_plan* plan, int32_t idx, int32_t ns_steps,
+                                              int32_t* fused) {
+    if (plan == nullptr || fused == nullptr || idx < 0 || idx >= (int32_t)plan->mats.size() || ns_steps < 0)
+        return DMUON_ERR_INVALID_ARG;
+    const MatPlan& mp = plan->mats[idx];
+    *fused = update_fused(plan->buckets[mp.bucket], mp, ns_steps) ? 1 : 0;
+    return DMUON_OK;
+}
+
 extern "C" dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t bucket, dmuon_tune_entry* out) {
     if (plan == nullptr || out == nullptr || bucket < 0 || bucket >= (int32_t)plan->buckets.size())
         return DMUON_ERR_INVALID_ARG;
@@ -316,6 +327,7 @@ extern "C" dmuon_status muon_plan_bucket_config(const dmuon_plan* plan, int32_t 
     e.algo = bp.algo;
     e.gram_restart = bp.seg_len;
     e.xcd_remap = bp.xcd_mask;
+    e.apply_pass = bp.apply_pass;
     e.cost_ms_per_matrix = bp.cost_ms;
     *out = e;
     return DMUON_OK;

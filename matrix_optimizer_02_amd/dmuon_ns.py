@@ -61,17 +61,19 @@ class TuneEntry(ctypes.Structure):
     """dmuon_tune_entry: how a plan runs a bucket of one (path, padded m, padded n)."""
     _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("padded_m", ctypes.c_int64),
                 ("padded_n", ctypes.c_int64), ("algo", ctypes.c_int32), ("gram_restart", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+                ("xcd_remap", ctypes.c_uint32), ("apply_pass", ctypes.c_int32),
                 ("cost_ms_per_matrix", ctypes.c_double)]
 
-    _KEYS = ("path", "tile", "padded_m", "padded_n", "algo", "gram_restart", "xcd_remap", "cost_ms_per_matrix")
+    _KEYS = ("path", "tile", "padded_m", "padded_n", "algo", "gram_restart", "xcd_remap", "apply_pass",
+             "cost_ms_per_matrix")
+    _OPTIONAL = {"apply_pass": 0}  # keys a cache file may lack, with their default
 
     def to_dict(self) -> dict:
         return {k: getattr(self, k) for k in self._KEYS}
 
     @classmethod
     def from_dict(cls, d: dict) -> "TuneEntry":
-        return cls(**{k: d[k] for k in cls._KEYS})
+        return cls(**{k: d[k] if k in d else cls._OPTIONAL[k] for k in cls._KEYS})
 
     def __repr__(self):
         return f"TuneEntry({self.to_dict()})"
@@ -102,6 +104,7 @@ def _load():
         "muon_plan_ex": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32, ctypes.POINTER(PlanOpts), vpp]),
         "muon_plan_bucket_algo": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p, c_int32_p]),
         "muon_plan_bucket_resident": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_int32_p]),
+        "muon_plan_update_fused": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, c_int32_p]),
         "muon_plan_bucket_config": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(TuneEntry)]),
         "muon_autotune_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.c_int32,
                                                          ctypes.POINTER(PlanOpts), ctypes.POINTER(ctypes.c_size_t)]),
@@ -251,6 +254,14 @@ class Plan:
         _check(_lib.muon_plan_bucket_resident(self._h, int(b), ctypes.byref(res)), "muon_plan_bucket_resident")
         return BucketEntry(path.value, pm.value, pn.value, cnt.value, tile.value, algo.value, restart.value,
                            bool(res.value))
+
+    def update_fused(self, idx: int, ns_steps: int = 5) -> bool:
+        """Whether a step of ns_steps iterations writes matrix idx's update from
+        its last B X launch (else the separate apply pass writes it)."""
+        res = ctypes.c_int32()
+        _check(_lib.muon_plan_update_fused(self._h, int(idx), int(ns_steps), ctypes.byref(res)),
+               "muon_plan_update_fused")
+        return bool(res.value)
 
     def config(self, b: int) -> TuneEntry:
         """The configuration bucket b runs with, as a tuning entry."""

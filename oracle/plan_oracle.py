@@ -102,6 +102,8 @@ def _apply_entry(bucket, e, option_restart, option="auto", shapes=()):
     remap = e.get("xcd_remap", XCD_REMAP_DEFAULT)
     if remap != XCD_REMAP_DEFAULT and remap & ~0xF:
         raise ValueError("remap bits")
+    if e.get("apply_pass", 0) not in (0, 1):
+        raise ValueError("apply_pass")
     if tile:
         bucket["tile"] = tile
     if (form == "gram_space" and option == "auto"
@@ -114,6 +116,7 @@ def _apply_entry(bucket, e, option_restart, option="auto", shapes=()):
         bucket["gram_restart"] = e["gram_restart"]
     if remap != XCD_REMAP_DEFAULT:
         bucket["xcd_remap"] = remap
+    bucket["apply_pass"] = e.get("apply_pass", 0)
     bucket["cost"] = e.get("cost_ms_per_matrix", 0.0)
 
 
@@ -147,7 +150,8 @@ def plan_reference(descs, algo: str = "auto", gram_restart: int = 0, tuned=None)
         restart = gram_restart if gram_restart > 0 else default_gram_restart(key[1])
         bk = {"path": key[0], "m_pad": key[1], "n_pad": key[2], "members": list(members[key]),
               "algo": form, "gram_restart": restart if form == "gram_space" else 1,
-              "tile": tile_granularity(key[0], key[1]), "xcd_remap": DEFAULT_XCD_REMAP, "cost": 0.0}
+              "tile": tile_granularity(key[0], key[1]), "xcd_remap": DEFAULT_XCD_REMAP, "apply_pass": 0,
+              "cost": 0.0}
         code = DTYPE_BF16 if key[0] == "bf16" else DTYPE_F32
         for e in tuned or []:
             if (e["path"], e["padded_m"], e["padded_n"]) == (code, key[1], key[2]):

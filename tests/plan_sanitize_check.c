@@ -87,7 +87,7 @@ int main(void) {
             tuned[t].algo = (int32_t)pick(0, 3); /* 3 is invalid */
             tuned[t].gram_restart = (int32_t)pick(-1, 4);
             tuned[t].xcd_remap = pick(0, 5) == 0 ? DMUON_XCD_REMAP_DEFAULT : (uint32_t)pick(0, 31);
-            tuned[t].reserved = pick(0, 20) == 0 ? 1 : 0;
+            tuned[t].apply_pass = (int32_t)pick(0, 20) == 0 ? 2 : (int32_t)pick(0, 1); /* 2 is invalid */
             tuned[t].cost_ms_per_matrix = (double)pick(0, 100) / 10.0;
         }
         dmuon_plan_opts opts;

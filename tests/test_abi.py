@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     names = build_mod.exported_symbols()
     assert set(names) == {"muon_plan", "muon_plan_ex", "muon_plan_workspace_bytes", "muon_plan_info",
                           "muon_plan_query", "muon_plan_bucket", "muon_plan_bucket_algo", "muon_plan_bucket_config",
-                          "muon_plan_bucket_resident",
+                          "muon_plan_bucket_resident", "muon_plan_update_fused",
                           "muon_autotune_workspace_bytes", "muon_autotune", "muon_plan_destroy",
                           "muon_step_batched", "muon_step_batched_noalloc",
                           "ns_orthogonalize_batched", "muon_step_batched_profiled", "muon_step_event_count",
@@ -173,15 +173,19 @@ def test_resident_buckets_by_hand():
     assert d.Plan([(128, 250, 1, 1), (128, 129, 1, 1)], "gram_space").bucket(0).algo == d.ALGO_GRAM_SPACE
 
 
-def _entry(path, m_pad, n_pad, tile=0, algo=0, restart=0, remap=0xFFFFFFFF, cost=0.0):
-    return {"path": path, "padded_m": m_pad, "padded_n": n_pad, "tile": tile, "algo": algo,
-            "gram_restart": restart, "xcd_remap": remap, "cost_ms_per_matrix": cost}
+def _entry(path, m_pad, n_pad, tile=0, algo=0, restart=0, remap=0xFFFFFFFF, cost=0.0, apply_pass=None):
+    e = {"path": path, "padded_m": m_pad, "padded_n": n_pad, "tile": tile, "algo": algo,
+         "gram_restart": restart, "xcd_remap": remap, "cost_ms_per_matrix": cost}
+    if apply_pass is not None:  # absent: the field's default (entries of older caches lack it)
+        e["apply_pass"] = apply_pass
+    return e
 
 
 TUNED_CASES = {
     # tile, form, restart and remap overrides on some buckets, dense-cost order kept
     "overrides": (CASES["mixed_odd"], [_entry(1, 512, 768, tile=128, remap=15), _entry(1, 256, 256, algo=2, restart=2),
-                                       _entry(1, 4096, 14336, algo=1, remap=0), _entry(0, 256, 512, tile=64),
+                                       _entry(1, 4096, 14336, algo=1, remap=0, apply_pass=1),
+                                       _entry(0, 256, 512, tile=64, apply_pass=0),
                                        _entry(1, 128, 640, restart=5), _entry(1, 999, 999, tile=128)]),
     # every bucket measured: ordered by count x cost, ties by first appearance
     "measured_order": ([(256, 512, 1, 1), (1024, 4096, 1, 1), (256, 512, 1, 1), (128, 128, 1, 1), (64, 64, 0, 0)],
@@ -209,8 +213,8 @@ def test_tuned_plan_matches_reference(name):
     for b, bk in enumerate(buckets):
         c = p.config(b)
         assert (c.path, c.padded_m, c.padded_n) == (0 if bk["path"] == "f32" else 1, bk["m_pad"], bk["n_pad"])
-        assert (c.tile, c.algo, c.gram_restart, c.xcd_remap) == (
-            bk["tile"], ALGO[bk["algo"]], bk["gram_restart"], bk["xcd_remap"]), b
+        assert (c.tile, c.algo, c.gram_restart, c.xcd_remap, c.apply_pass) == (
+            bk["tile"], ALGO[bk["algo"]], bk["gram_restart"], bk["xcd_remap"], bk["apply_pass"]), b
         assert c.cost_ms_per_matrix == bk["cost"]
         assert p.bucket(b).tile == bk["tile"]
 
@@ -219,7 +223,8 @@ def test_tuned_plan_matches_reference(name):
                                  _entry(1, 512, 768, tile=384), _entry(0, 256, 512, tile=128),
                                  _entry(0, 256, 512, algo=2), _entry(1, 512, 768, algo=3),
                                  _entry(1, 512, 768, restart=-1), _entry(1, 512, 768, remap=16),
-                                 _entry(1, 512, 768, cost=-1.0)])
+                                 _entry(1, 512, 768, cost=-1.0), _entry(1, 512, 768, apply_pass=2),
+                                 _entry(1, 512, 768, apply_pass=-1)])
 def test_invalid_tuned_entries_rejected(bad):
     descs = CASES["mixed_odd"]
     with pytest.raises(ValueError):
@@ -512,3 +517,30 @@ def test_binding_tensor_checks(monkeypatch):
     monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
     with pytest.raises(ValueError, match=r"grads\[0\] is on another device"):
         d._check_tensors(plan, good["grad"], "grads", "grad")
+
+
+def test_update_fused_by_hand():
+    # the last B X launch writes a bf16 parameter's update when cols % 8 == 0 and its
+    # bucket runs tiled bf16 launches with apply_pass 0; ns_steps 0 has no B X at all
+    descs = [(1024, 4096, 1, 1), (4096, 1024, 1, 1), (520, 300, 1, 1), (384, 1000, 1, 0), (120, 256, 1, 1),
+             (256, 512, 0, 0), (128, 640, 1, 1), (300, 520, 1, 1), (264, 136, 1, 1)]
+    want = [True, True, False, False, False, False, True, True, True]
+    p = d.Plan(descs)
+    assert [p.update_fused(i) for i in range(len(descs))] == want
+    assert not any(p.update_fused(i, 0) for i in range(len(descs)))
+    assert [p.update_fused(i, 1) for i in range(len(descs))] == want
+    # apply_pass 1 on one bucket sends its members (1024 x 4096 and its transpose)
+    # through the apply pass
+    e = p.config(p.query(0).bucket)
+    e.apply_pass = 1
+    q = d.Plan(descs, tuning=[e])
+    assert [q.update_fused(i) for i in range(len(descs))] == [False, False] + want[2:]
+    # forced onto the Gram space, the 128 x 256 bucket is no longer resident
+    g = d.Plan(descs, "gram_space")
+    assert p.bucket(p.query(4).bucket).resident and g.update_fused(4)
+    res = ctypes.c_int32()
+    assert LIB.muon_plan_update_fused(None, 0, 5, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_update_fused(p.handle, len(descs), 5, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_update_fused(p.handle, -1, 5, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_update_fused(p.handle, 0, -1, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
+    assert LIB.muon_plan_update_fused(p.handle, 0, 5, None) == d.DMUON_ERR_INVALID_ARG

@@ -84,21 +84,37 @@ def test_resident_counts_whole_products():
     assert ex == {"gram": 5 * 2 * m * m * n, "square": 5 * 2 * m ** 3, "prod": 0, "bx": 5 * 2 * m * m * n}
 
 
+def test_bx_flops_by_iteration():
+    # a matrix's closing product runs where its segments end; resident ones none
+    from matrix_optimizer_02_amd.workloads import custom_workload
+
+    w = custom_workload("t", [(256, 1024), (512, 512), (1024, 256), (128, 256)])
+    by = bench.bx_flops_by_iteration(w, [3, 1, 2, 1], [False, False, False, True])
+    a, b, c = bench.bx_flops(256, 1024), bench.bx_flops(512, 512), bench.bx_flops(256, 1024)
+    assert by == [b, b + c, a + b, b + c, a + b + c]
+    # the per-phase totals agree with executed_flops
+    tot = sum(bench.executed_flops(min(s.rows, s.cols), max(s.rows, s.cols), L)["bx"]
+              for s, L in zip(w.matrices[:3], [3, 1, 2]))
+    assert sum(by) == tot
+
+
 def test_dominant_kernel_choice():
-    # grouped buckets restarting every 3 and every 2 iterations plus a short-side one:
-    # B X launches in iterations 0 .. 4 (short side every iteration)
     rows = [[1.0, 2.0, 3.0, 4.0, 5.0], [1.0, 2.0, 3.0, 4.0, 5.0]]
-    k, ms, fl = bench.dominant_kernel([3, 2, 1], [False, False, False], 50.0, 0, rows, 9.0, False)
-    assert "bf16" in k and ms == 3.0 and fl == 10.0
+    # a short-side bucket: B X launches in iterations 0 .. 4
+    k, ms, fl, it = bench.dominant_kernel([10, 10, 10, 10, 10], False, 0, rows, 9.0, False)
+    assert "bf16" in k and ms == 3.0 and fl == 10.0 and it == [0, 1, 2, 3, 4]
     # Gram space only, every 3 iterations: segments close in iterations 2 and 4
-    k, ms, fl = bench.dominant_kernel([3, 3], [False, False], 40.0, 0, rows, 9.0, False)
-    assert ms == 4.0 and fl == 20.0
-    # fp32 only: the SIMT kernel
-    k, ms, fl = bench.dominant_kernel([1], [False], 50.0, 0, rows, 9.0, True)
+    k, ms, fl, it = bench.dominant_kernel([0, 0, 20, 0, 20], False, 0, rows, 9.0, False)
+    assert ms == 4.0 and fl == 20.0 and it == [2, 4]
+    # the last launch writes the updates: an instance of its own, timed apart
+    k, ms, fl, it = bench.dominant_kernel([10, 10, 30, 10, 40], True, 0, rows, 9.0, False)
+    assert ms == 2.5 and fl == 15.0 and it == [0, 1, 2, 3] and "plain" in k
+    # ... unless it is the only one
+    k, ms, fl, it = bench.dominant_kernel([0, 0, 0, 0, 20], True, 0, rows, 9.0, False)
+    assert ms == 5.0 and fl == 20.0 and it == [4]
+    # fp32 only: the fp32 matrix-core kernel
+    k, ms, fl, it = bench.dominant_kernel([10, 10, 10, 10, 10], False, 0, rows, 9.0, True)
     assert "f32" in k and ms == 3.0
     # every bucket resident: the resident launch, timed inside iteration 0's Gram phase
-    k, ms, fl = bench.dominant_kernel([1, 1], [True, True], 0.0, 7.0, rows, 9.0, False)
-    assert "resident" in k and ms == 9.0 and fl == 7.0
-    # resident buckets beside grouped ones leave the B X accounting to the grouped ones
-    k, ms, fl = bench.dominant_kernel([1, 3], [True, False], 30.0, 7.0, rows, 9.0, False)
-    assert "bf16" in k and ms == 4.0 and fl == 15.0
+    k, ms, fl, it = bench.dominant_kernel([0, 0, 0, 0, 0], False, 7.0, rows, 9.0, False)
+    assert "resident" in k and ms == 9.0 and fl == 7.0 and it == []
