@@ -631,8 +631,11 @@ def main(argv=None):
     seg_len = [plan.bucket(plan.query(i).bucket).gram_restart for i in range(w.count)]
     gram_space = [plan.bucket(plan.query(i).bucket).algo == d.ALGO_GRAM_SPACE for i in range(w.count)]
     resident = [plan.bucket(plan.query(i).bucket).resident for i in range(w.count)]
-    # matrices whose update the last B X launch writes (the apply pass skips them)
+    # matrices whose update the kernel ending their iteration writes (the apply
+    # pass skips them): the last B X launch, or the resident kernel
     fused = [plan.update_fused(i, NS_STEPS) for i in range(w.count)]
+    fused_bx = [f and not r for f, r in zip(fused, resident)]
+    fused_res = [f and r for f, r in zip(fused, resident)]
     alg = dense = 0
     execd = {"gram": 0, "square": 0, "prod": 0, "bx": 0}  # grouped launches
     res_flops = 0  # the resident kernel's (every iteration of a small bucket in one launch)
@@ -656,7 +659,7 @@ def main(argv=None):
     assert sum(bx_by_iter) == execd["bx"]
     bx_rows = [[p[names.index(f"bx{k}")] for k in range(NS_STEPS)] for p in per]
     kernel, launch_ms, flops_per_launch, bx_plain = dominant_kernel(
-        bx_by_iter, any(fused), res_flops, bx_rows, avg["gram0"], f32_only)
+        bx_by_iter, any(fused_bx), res_flops, bx_rows, avg["gram0"], f32_only)
     achieved = flops_per_launch / (launch_ms / 1e3) / 1e12
     traffic = (read_traffic("bx_gemm_bf16_llama8b")
                if args.workload == "llama3.1-8b_owner_1of8" and not args.tuning_cache else None)
@@ -708,10 +711,11 @@ def main(argv=None):
     gsz = 2 if paths == {"bf16"} else 4
     psz = 2 if all(s.param_dtype == "bf16" for s in w.matrices) else 4
     prep_bytes = elems * (gsz + 4 + 4 + gsz)   # read G, M; write M', U (as X)
-    # the apply pass: read O (X), W; write W' -- for the matrices the last B X does not update
+    # the apply pass: read O (X), W; write W' -- for the matrices no other kernel updates
     psize = lambda s: 2 if s.param_dtype == "bf16" else 4
     apply_bytes = sum(s.rows * s.cols * (gsz + 2 * psize(s)) for s, f in zip(w.matrices, fused) if not f)
-    fused_elems = sum(s.rows * s.cols for s, f in zip(w.matrices, fused) if f)
+    fused_elems = sum(s.rows * s.cols for s, f in zip(w.matrices, fused_bx) if f)
+    res_upd = [s for s, f in zip(w.matrices, fused_res) if f]
 
     def rate(nbytes, ms):
         if nbytes == 0 or ms <= 0:
@@ -722,21 +726,27 @@ def main(argv=None):
         "prep": {"bytes": prep_bytes, "ms": round(avg["prep"], 4), **rate(prep_bytes, avg["prep"])},
         "apply": {"bytes": apply_bytes, "ms": round(avg["apply"], 4), **rate(apply_bytes, avg["apply"]),
                   "matrices": w.count - sum(fused)},
-        "update_in_last_bx": {"matrices": sum(fused), "elements": fused_elems,
+        "update_in_last_bx": {"matrices": sum(fused_bx), "elements": fused_elems,
                               "bytes": fused_elems * 4,
                               "note": "read W, write W' (bf16) from the last B X launch's epilogue; "
                                       "the final X never goes to HBM, so the apply pass's 6 bytes "
                                       "per element become 4, inside that launch"},
+        "update_in_resident": {"matrices": len(res_upd),
+                               "elements": sum(s.rows * s.cols for s in res_upd),
+                               "bytes": sum(s.rows * s.cols * 2 * psize(s) for s in res_upd),
+                               "note": "read W, write W' from the resident kernel's final X in LDS, "
+                                       "which also sums its matrices' norm partials: no finalize or "
+                                       "apply launch for them"},
     }
     last = NS_STEPS - 1
-    if any(fused) and bx_by_iter[last] > 0 and last not in bx_plain:
+    if any(fused_bx) and bx_by_iter[last] > 0 and last not in bx_plain:
         last_ms = sum(r[last] for r in bx_rows) / len(bx_rows)
         out["bx_update_launch"] = {
             "kernel": "ns_gemm_bf16_kernel<256, BX, fused update>: the last iteration's B X, whose epilogue "
                       "writes W' for the matrices it updates",
             "ms": round(last_ms, 4), "flops": bx_by_iter[last],
             "tflops": round(bx_by_iter[last] / (last_ms / 1e3) / 1e12, 1),
-            "update_bytes": fused_elems * 4, "matrices": sum(fused)}
+            "update_bytes": fused_elems * 4, "matrices": sum(fused_bx)}
     out["graph"] = graph_bench(d, plan, G, M, W, ws, max(args.steps, 50 if ms_per_step < 5 else 0), w.count)
     if tuning_info is not None:
         out["tuning"] = tuning_info

@@ -143,9 +143,11 @@ typedef struct {
     uint32_t xcd_remap;      /* bf16 path: bit per phase (1 Gram, 2 square, 4 B X, 8 prod) whose launch
                                 gives each XCD a contiguous run of the bucket's tiles (neighbouring tiles
                                 share operand panels in that XCD's L2); DMUON_XCD_REMAP_DEFAULT: B X only */
-    int32_t apply_pass;      /* 0 (default): on the bf16 path, the last B X launch writes the update
-                                (or the output) of every member with a bf16 parameter (output) and
-                                cols a multiple of 8 from its epilogue, and X is never written back;
+    int32_t apply_pass;      /* 0 (default): the kernel that ends the iteration writes the update (or
+                                the output) and X is never written back: in a resident bucket the
+                                resident kernel, for every member; otherwise, on the bf16 path, the
+                                last B X launch's epilogue, for every member with a bf16 parameter
+                                (output) and cols a multiple of 8;
                                 1: a separate elementwise pass writes it from the final X for every
                                 member, as it does for the other members.  The two give identical
                                 bits; other values are INVALID_ARG */
@@ -250,17 +252,18 @@ DMUON_API dmuon_status muon_plan_bucket_algo(const dmuon_plan* plan, int32_t buc
 DMUON_API dmuon_status muon_plan_bucket_resident(const dmuon_plan* plan, int32_t bucket, int32_t* resident);
 
 /* Where a step (or orthogonalisation) with ns_steps iterations writes matrix
- * idx's update (output): 1 from the epilogue of its last B X launch, which
+ * idx's update (output): 1 from the kernel that ends its iteration, which
  * then never writes the final X back, 0 in the separate elementwise pass.
  * The owner applies the update right after the matrix's Newton-Schulz
  * iteration (DMuon abstract; DMuon explainer on gist.science, section 2.1
- * Owner-Centric Executiestrategie); written by the product that ends the
+ * Owner-Centric Executiestrategie); written by the kernel that ends the
  * iteration, the orthogonalised matrix makes no round trip through memory.
- * The epilogue takes a bf16 parameter (output) with cols a multiple of 8
- * whose bucket runs tiled bf16 launches (not resident) and whose
- * configuration has apply_pass 0, when ns_steps > 0; the two routes give
- * identical bits.  Host only.  Errors: INVALID_ARG (null plan or fused, idx
- * out of range, ns_steps < 0). */
+ * With ns_steps > 0 and the bucket's apply_pass 0: the resident kernel takes
+ * every member of a resident bucket (muon_plan_bucket_resident), any
+ * parameter type and shape; the last B X launch's epilogue takes a bf16
+ * parameter (output) with cols a multiple of 8 in a bucket of tiled bf16
+ * launches.  The two routes give identical bits.  Host only.  Errors:
+ * INVALID_ARG (null plan or fused, idx out of range, ns_steps < 0). */
 DMUON_API dmuon_status muon_plan_update_fused(const dmuon_plan* plan, int32_t idx, int32_t ns_steps,
                                               int32_t* fused);
 
@@ -307,9 +310,9 @@ DMUON_API void muon_plan_destroy(dmuon_plan* plan);
  * place in momenta[i], fp32), normalisation, ns_steps NS iterations on the
  * short side (or in the Gram space, per bucket: dmuon_algo), and the
  * in-place parameter update of params[i] (param_dtype; bf16 results are
- * rounded to nearest even once, from fp32), written by the last B X
- * launch's epilogue where muon_plan_update_fused says so, else by an
- * elementwise pass.
+ * rounded to nearest even once, from fp32), written by the kernel that
+ * ends the iteration (resident kernel, or last B X launch) where
+ * muon_plan_update_fused says so, else by an elementwise pass.
  *   grads[i]   device, rows x cols, grad_dtype, read only, must not alias
  *   momenta[i] device, rows x cols, fp32, read and written
  *   params[i]  device, rows x cols, param_dtype, read and written

@@ -305,13 +305,18 @@ dmuon_status run_impl(const dmuon_plan* p, const StepParams& sp, void* workspace
     pa.has_momentum = sp.mom ? 1 : 0;
     pa.total_blocks = prep_blocks;
     if (launch_prep(pa, stream) != hipSuccess) return DMUON_ERR_HIP;
-    if (launch_finalize_norms(table, count, partials, scale, sp.eps, stream) != hipSuccess)
+    // the resident kernel sums its matrices' partials itself; the others read
+    // the scale array
+    bool need_scale = false;
+    for (size_t b = 0; b < nb; ++b) need_scale = need_scale || !resident[b];
+    if (need_scale && launch_finalize_norms(table, count, partials, scale, sp.eps, stream) != hipSuccess)
         return DMUON_ERR_HIP;
     if (!mark()) return DMUON_ERR_HIP;
     // the resident buckets' whole iteration (timed with iteration 0's Gram phase)
-    if (!resident_list.empty() &&
-        launch_resident(table, ws, scale, sp.a, sp.b, sp.c, steps, resident_list, stream) != hipSuccess)
-        return DMUON_ERR_HIP;
+    if (!resident_list.empty()) {
+        ResidentStep rs{partials, sp.eps, sp.a, sp.b, sp.c, steps, sp.update, sp.lr, sp.wd};
+        if (launch_resident(table, ws, rs, resident_list, stream) != hipSuccess) return DMUON_ERR_HIP;
+    }
 
     // The iterations as segments of seg[b] iterations per bucket (1: the
     // short side).  Iteration k is position j = k mod L of its segment, whose

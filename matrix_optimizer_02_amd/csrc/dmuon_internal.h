@@ -150,18 +150,22 @@ struct DevMatRec {
     int32_t src_dtype, dst_dtype, path;
     float upd_scale;       // sqrt(max(1, rows / cols))
     int32_t final_copy;    // X copy (0 | 1) that holds the orthogonalised matrix
-    int32_t fused;         // 1: the last B X launch writes dst (update or output) from its
-                           // epilogue; X is not written back and the apply pass skips it
+    int32_t fused;         // 1: the kernel ending the iteration (the last B X launch's
+                           // epilogue, or the resident kernel) writes dst (update or
+                           // output); X is not written back and the apply pass skips it
 };
 
 // Whether a step with `steps` iterations writes matrix mp's update from the
-// epilogue of its last B X launch (else the apply pass writes it): a bf16
-// parameter with cols a multiple of 8 (16-byte chunks of whole rows), in a bf16
-// bucket of tiled launches (not resident) that keeps the default route.
+// kernel that finishes its iterations (else the apply pass writes it), in a
+// bucket that keeps the default route: the resident kernel writes any
+// parameter of its buckets; the last B X launch writes a bf16 parameter with
+// cols a multiple of 8 (16-byte chunks of whole rows) of a bf16 bucket of
+// tiled launches.
 inline bool update_fused(const BucketPlan& bp, const MatPlan& mp, int32_t steps) {
+    if (steps <= 0 || bp.apply_pass != 0) return false;
     const bool resident = bp.algo == DMUON_ALGO_SHORT_SIDE && resident_shape(bp.path, bp.m_pad, bp.n_pad);
-    return steps > 0 && bp.path == kPathBF16 && !resident && bp.apply_pass == 0 &&
-           mp.param_dtype == DMUON_BF16 && mp.cols % 8 == 0;
+    if (resident) return true;
+    return bp.path == kPathBF16 && mp.param_dtype == DMUON_BF16 && mp.cols % 8 == 0;
 }
 
 // Apply kernel: each block covers kApplyElems elements of the real matrix.

@@ -100,12 +100,138 @@ struct ResidentSeg {
 struct ResidentArgs {
     const DevMatRec* recs;
     char* ws;
-    const float* scale;
-    float a, b, c;
+    const float* partials;
+    float eps, a, b, c;
     int32_t steps;
+    int32_t update;
+    float lr, wd;
     int32_t nseg;
     ResidentSeg seg[kMaxSeg];
 };
+
+// Per thread, kB 16-byte chunks of X are moved at a time, their global loads
+// all issued before the first is used.  The chunk count (16 n_pad) is a
+// multiple of kThreads but not always of kB kThreads: an index past the end
+// is taken modulo the count, which repeats a chunk of the same batch
+// (straight-line code, no branch between the loads).
+constexpr int kB = 8;
+__device__ __forceinline__ int wrap(int q, int total) { return q < total ? q : q - total; }
+
+// The parameter (or output) of a fused record, from the final X in LDS: O is X
+// for a wide matrix and X^T for a tall one; W' = keep W + coef O element by
+// element with coef = -lr sqrt(max(1, rows / cols)) and keep = 1 - lr wd,
+// rounded once to the parameter's type (the apply pass's arithmetic), or
+// O itself without the update.  A chunk is 8 consecutive elements of a
+// parameter row; a tall matrix's chunks are columns of X, read with the
+// transposing LDS read by groups of 16 lanes (16 parameter rows, one 8-column
+// block).  VEC (cols a multiple of 8): 16- or 32-byte accesses per chunk;
+// otherwise element by element.  Chunks outside the matrix (padding, or a
+// repeated index) load from element 0 and store nothing.
+template <typename DT, bool TALL, bool VEC>
+__device__ __forceinline__ void write_param(const char* X, int xrow, int n, const DevMatRec& rec,
+                                            const ResidentArgs& args, int tid) {
+    constexpr bool kBF = sizeof(DT) == 2;
+    const int rows = rec.rows, cols = rec.cols;  // rows cols <= kM kMaxN: int offsets
+    DT* const W = static_cast<DT*>(rec.dst);
+    const bool update = args.update != 0;
+    const float coef = -args.lr * rec.upd_scale;
+    const float keep = 1.0f - args.lr * args.wd;
+    const int total = kM * n / 8;
+    const int t16 = tid & 15;
+    for (int q0 = 0; q0 < total; q0 += kB * kThreads) {
+        u32x4_t o[kB];
+        int off[kB], pcol[kB];
+        bool ok[kB];
+        u32x4_t wb[kB];       // VEC, bf16
+        f32x4_t wf[kB][2];    // VEC, fp32
+        float ws[kB][8];      // element by element
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int qr = q0 + u * kThreads + tid;
+            const int q = wrap(qr, total);
+            int prow;
+            if (!TALL) {
+                prow = q / (n / 8);
+                pcol[u] = 8 * (q % (n / 8));
+                o[u] = *reinterpret_cast<const u32x4_t*>(X + loff(prow, pcol[u], xrow));
+            } else {
+                // group q / 16: parameter rows 16 (gq / 16) + t16, columns 8 (gq % 16) ..
+                const int gq = q >> 4;
+                const int k0 = 8 * (gq & 15), r0 = 16 * (gq >> 4);
+                prow = r0 + t16;
+                pcol[u] = k0;
+                shortx4 hv[2];
+                #pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_shortx4*)((__attribute__((address_space(3))) char*)X +
+                                       loff(k0 + 4 * hh + (t16 >> 2), r0 + 4 * (t16 & 3), xrow)));
+                o[u] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                // every lane takes part in the transposing reads: keep them
+                // out of the branches below
+                asm volatile("" : "+v"(o[u]));
+            }
+            ok[u] = qr < total && prow < rows && pcol[u] < cols;
+            off[u] = ok[u] ? prow * cols + pcol[u] : 0;
+        }
+        if (update) {
+            #pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                if (VEC) {
+                    if constexpr (kBF) {
+                        wb[u] = ld_stream<u32x4_t>(W + off[u]);
+                    } else {
+                        wf[u][0] = ld_stream<f32x4_t>(W + off[u]);
+                        wf[u][1] = ld_stream<f32x4_t>(W + off[u] + 4);
+                    }
+                } else {
+                    #pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        ws[u][e] = Elem<DT>::load(W + (ok[u] && pcol[u] + e < cols ? off[u] + e : 0));
+                }
+            }
+        }
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (!ok[u]) continue;
+            float v[8];
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = __uint_as_float(o[u][e] << 16);
+                v[2 * e + 1] = __uint_as_float(o[u][e] & 0xffff0000u);
+            }
+            if (update) {
+                float w[8];
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (!VEC) w[e] = ws[u][e];
+                    else if constexpr (kBF)
+                        w[e] = (e & 1) ? __uint_as_float(wb[u][e / 2] & 0xffff0000u) : __uint_as_float(wb[u][e / 2] << 16);
+                    else w[e] = wf[u][e / 4][e % 4];
+                }
+                #pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fmaf(coef, v[e], keep * w[e]);
+            }
+            DT* const dst = W + off[u];
+            if (VEC) {
+                if constexpr (kBF) {
+                    u32x4_t s;
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[e] = (uint32_t)f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16);
+                    st_stream<u32x4_t>(dst, s);
+                } else {
+                    st_stream<f32x4_t>(dst, f32x4_t{v[0], v[1], v[2], v[3]});
+                    st_stream<f32x4_t>(dst + 4, f32x4_t{v[4], v[5], v[6], v[7]});
+                }
+            } else {
+                #pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (pcol[u] + e < cols) Elem<DT>::store(dst + e, v[e]);
+            }
+        }
+    }
+}
 
 __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs args) {
     __shared__ __attribute__((aligned(1024))) char smem[kXBytes + kABytes];
@@ -123,17 +249,37 @@ __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31, khalf = lane >> 5;
 
-    // X (the prepared U, copy 0) into LDS
+    // s = 1 / (||U||_F + eps) from the record's norm partials, summed as
+    // finalize_norms sums them (there: thread t adds partials t, t + 256, ..,
+    // the waves reduce by butterfly and thread 0 adds the wave sums in order;
+    // with at most 64 partials only wave 0's sum is nonzero, so every lane of
+    // each wave here forms the same value bit for bit)
+    static_assert((kM / kPrepTile) * (kMaxN / kPrepTile) <= 64, "one partial a lane");
+    const int np = (rec.r_pad / kPrepTile) * (rec.c_pad / kPrepTile);
+    float nsum = 0.f;
+    if (lane < np) nsum += args.partials[rec.partial_off + lane];
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nsum += __shfl_xor(nsum, off, 64);
+    const float s0 = 1.0f / (sqrtf(nsum) + args.eps);
+
+    // X (the prepared U, copy 0) into LDS, kB loads in flight per thread (a
+    // repeated chunk is stored twice, with the same bytes)
     const uint4* xg = reinterpret_cast<const uint4*>(args.ws + rec.x_off0);
     const int chunks = kM * n / 8;
-    for (int q = tid; q < chunks; q += kThreads) {
-        const int r = q / (n / 8), c = 8 * (q % (n / 8));
-        *reinterpret_cast<uint4*>(X + loff(r, c, xrow)) = xg[q];
+    for (int q0 = 0; q0 < chunks; q0 += kB * kThreads) {
+        uint4 xv[kB];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) xv[u] = xg[wrap(q0 + u * kThreads + tid, chunks)];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int q = wrap(q0 + u * kThreads + tid, chunks);
+            *reinterpret_cast<uint4*>(X + loff(q / (n / 8), 8 * (q % (n / 8)), xrow)) = xv[u];
+        }
     }
 
     const float a = args.a, b = args.b, c = args.c;
     for (int it = 0; it < args.steps; ++it) {
-        const float sc = it == 0 ? args.scale[pi] : 1.0f;
+        const float sc = it == 0 ? s0 : 1.0f;
         __syncthreads();  // X' complete; every wave done with B'
 
         // ---- A = s^2 X X^T, stored transposed (A is symmetric) -------------------
@@ -248,7 +394,24 @@ __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs a
     }
     __syncthreads();
 
-    // the result into the X copy that the apply pass reads
+    if (rec.fused) {
+        const bool tall = rec.transposed != 0, vec = (rec.cols & 7) == 0;
+#define DMUON_WRITE(DT)                                                          \
+        do {                                                                     \
+            if (tall) {                                                          \
+                if (vec) write_param<DT, true, true>(X, xrow, n, rec, args, tid);   \
+                else write_param<DT, true, false>(X, xrow, n, rec, args, tid);      \
+            } else {                                                             \
+                if (vec) write_param<DT, false, true>(X, xrow, n, rec, args, tid);  \
+                else write_param<DT, false, false>(X, xrow, n, rec, args, tid);     \
+            }                                                                    \
+        } while (0)
+        if (rec.dst_dtype == DMUON_BF16) DMUON_WRITE(uint16_t);
+        else DMUON_WRITE(float);
+#undef DMUON_WRITE
+        return;
+    }
+    // else the result into the X copy that the apply pass reads
     uint4* xo = reinterpret_cast<uint4*>(args.ws + (rec.final_copy ? rec.x_off1 : rec.x_off0));
     for (int q = tid; q < chunks; q += kThreads) {
         const int r = q / (n / 8), c8 = 8 * (q % (n / 8));
@@ -258,16 +421,20 @@ __global__ __launch_bounds__(kThreads, 1) void ns_resident_kernel(ResidentArgs a
 
 }  // namespace
 
-hipError_t launch_resident(const DevMatRec* recs, char* ws, const float* scale, float a, float b, float c,
-                           int32_t steps, const std::vector<ResidentBucket>& buckets, hipStream_t stream) {
+hipError_t launch_resident(const DevMatRec* recs, char* ws, const ResidentStep& st,
+                           const std::vector<ResidentBucket>& buckets, hipStream_t stream) {
     ResidentArgs ra{};
     ra.recs = recs;
     ra.ws = ws;
-    ra.scale = scale;
-    ra.a = a;
-    ra.b = b;
-    ra.c = c;
-    ra.steps = steps;
+    ra.partials = st.partials;
+    ra.eps = st.eps;
+    ra.a = st.a;
+    ra.b = st.b;
+    ra.c = st.c;
+    ra.steps = st.steps;
+    ra.update = st.update;
+    ra.lr = st.lr;
+    ra.wd = st.wd;
     auto flush = [&]() -> hipError_t {
         if (ra.nseg == 0) return hipSuccess;
         const int total = ra.seg[ra.nseg - 1].first_block + ra.seg[ra.nseg - 1].count;

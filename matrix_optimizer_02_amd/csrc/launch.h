@@ -140,8 +140,18 @@ struct ResidentBucket {
 };
 
 // All ns_steps (> 0) iterations of the given buckets' matrices: X from each
-// record's copy 0, the result into its copy final_copy.
-hipError_t launch_resident(const DevMatRec* recs, char* ws, const float* scale, float a, float b, float c,
-                           int32_t steps, const std::vector<ResidentBucket>& buckets, hipStream_t stream);
+// record's copy 0, the normalisation from the record's norm partials (summed
+// as finalize_norms sums them), and the result into the parameter (update, or
+// output: W' as the apply pass computes it) for a fused record, else into the
+// X copy final_copy.
+struct ResidentStep {
+    const float* partials;
+    float eps, a, b, c;
+    int32_t steps;
+    int32_t update;  // 1: W' = W (1 - lr wd) - lr s O ; 0: dst = O
+    float lr, wd;
+};
+hipError_t launch_resident(const DevMatRec* recs, char* ws, const ResidentStep& st,
+                           const std::vector<ResidentBucket>& buckets, hipStream_t stream);
 
 }  // namespace dmuon

@@ -257,7 +257,8 @@ class Plan:
 
     def update_fused(self, idx: int, ns_steps: int = 5) -> bool:
         """Whether a step of ns_steps iterations writes matrix idx's update from
-        its last B X launch (else the separate apply pass writes it)."""
+        the kernel that ends its iteration, the resident kernel or its last B X
+        launch (else the separate apply pass writes it)."""
         res = ctypes.c_int32()
         _check(_lib.muon_plan_update_fused(self._h, int(idx), int(ns_steps), ctypes.byref(res)),
                "muon_plan_update_fused")

@@ -520,24 +520,32 @@ def test_binding_tensor_checks(monkeypatch):
 
 
 def test_update_fused_by_hand():
-    # the last B X launch writes a bf16 parameter's update when cols % 8 == 0 and its
-    # bucket runs tiled bf16 launches with apply_pass 0; ns_steps 0 has no B X at all
+    # with apply_pass 0: the resident kernel writes every member of a resident
+    # bucket (any parameter type, any cols); the last B X launch writes a bf16
+    # parameter's update when cols % 8 == 0 and its bucket runs tiled bf16
+    # launches; ns_steps 0 has no iteration at all
     descs = [(1024, 4096, 1, 1), (4096, 1024, 1, 1), (520, 300, 1, 1), (384, 1000, 1, 0), (120, 256, 1, 1),
-             (256, 512, 0, 0), (128, 640, 1, 1), (300, 520, 1, 1), (264, 136, 1, 1)]
-    want = [True, True, False, False, False, False, True, True, True]
+             (256, 512, 0, 0), (128, 640, 1, 1), (300, 520, 1, 1), (264, 136, 1, 1), (100, 250, 1, 0),
+             (250, 100, 1, 0)]
+    want = [True, True, False, False, True, False, True, True, True, True, True]
     p = d.Plan(descs)
+    assert [p.bucket(p.query(i).bucket).resident for i in (4, 9, 10)] == [True] * 3
+    assert not any(p.bucket(p.query(i).bucket).resident for i in (0, 2, 6, 8))
     assert [p.update_fused(i) for i in range(len(descs))] == want
     assert not any(p.update_fused(i, 0) for i in range(len(descs)))
     assert [p.update_fused(i, 1) for i in range(len(descs))] == want
-    # apply_pass 1 on one bucket sends its members (1024 x 4096 and its transpose)
-    # through the apply pass
-    e = p.config(p.query(0).bucket)
-    e.apply_pass = 1
-    q = d.Plan(descs, tuning=[e])
-    assert [q.update_fused(i) for i in range(len(descs))] == [False, False] + want[2:]
-    # forced onto the Gram space, the 128 x 256 bucket is no longer resident
+    # apply_pass 1 on one bucket sends its members through the apply pass: the
+    # 1024 x 4096 one (and its transpose), then the resident 128 x 256 one
+    for i, members in ((0, (0, 1)), (9, (4, 9, 10))):
+        e = p.config(p.query(i).bucket)
+        e.apply_pass = 1
+        q = d.Plan(descs, tuning=[e])
+        assert [q.update_fused(k) for k in range(len(descs))] == [w and k not in members for k, w in enumerate(want)]
+    # forced onto the Gram space, the 128 x 256 bucket is no longer resident: its
+    # bf16 parameter with cols 256 stays fused, the others fall back to the apply pass
     g = d.Plan(descs, "gram_space")
-    assert p.bucket(p.query(4).bucket).resident and g.update_fused(4)
+    assert not g.bucket(g.query(4).bucket).resident
+    assert [g.update_fused(i) for i in (4, 9, 10)] == [True, False, False]
     res = ctypes.c_int32()
     assert LIB.muon_plan_update_fused(None, 0, 5, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG
     assert LIB.muon_plan_update_fused(p.handle, len(descs), 5, ctypes.byref(res)) == d.DMUON_ERR_INVALID_ARG

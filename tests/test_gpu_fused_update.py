@@ -1,17 +1,23 @@
-"""GPU checks of the update written by the last B X launch's epilogue.
+"""GPU checks of the update written by the kernel that ends the iteration.
 
-By default the last B X launch writes the update (or, for the orthogonalisation
-entry point, the output) of every bf16 parameter whose bucket runs the tiled
+By default the resident kernel writes the update (or, for the orthogonalisation
+entry point, the output) of every member of a resident bucket, and the last
+B X launch's epilogue that of every bf16 parameter whose bucket runs the tiled
 bf16 products and whose cols is a multiple of 8; the apply pass writes the
 others.  A tuning entry with apply_pass = 1 sends every member of its bucket
 through the apply pass instead.  Both routes compute W' = W (1 - lr wd) -
 lr s O from the same bf16 O, so they must agree bit for bit; the oracle parity
-of the default route is covered by the step tests.
+of the default route is covered by the step tests.  The resident kernel also
+sums the norm partials itself, so its matrices' normalisation is checked
+against the separate finalize pass here as well.
 
-The set mixes wide and tall (transposed) matrices, ragged sides, Gram-space
-and short-side buckets, tile 128 and 256, a resident bucket, an fp32
-parameter and a tall matrix whose cols is not a multiple of 8 (the last three
-take the apply pass either way).
+The tiled set mixes wide and tall (transposed) matrices, ragged sides,
+Gram-space and short-side buckets and tile 128 and 256, with an fp32 parameter
+and a tall matrix whose cols is not a multiple of 8 (those two take the apply
+pass either way).  The resident buckets (padded 128 x 128, 128 x 256 and
+128 x 384 or 128 x 512) hold wide and tall matrices with bf16 and fp32
+parameters, with cols a multiple of 8 (16-byte chunks) and not (element by
+element).
 """
 
 import sys
@@ -26,7 +32,11 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(1024, 4096, "bf16"), (4096, 1024, "bf16"), (300, 520, "bf16"), (520, 300, "bf16"),
           (1000, 384, "bf16"), (384, 1000, "f32"), (2048, 2048, "bf16"), (128, 640, "bf16"),
-          (640, 128, "bf16"), (100, 250, "bf16"), (264, 136, "bf16")]
+          (640, 128, "bf16"), (264, 136, "bf16"),
+          # resident buckets
+          (100, 250, "bf16"), (250, 100, "bf16"), (120, 256, "bf16"), (250, 100, "f32"), (128, 512, "f32"),
+          (384, 96, "f32"), (512, 128, "bf16"), (128, 128, "bf16"), (77, 77, "f32")]
+RESIDENT = SHAPES[10:]
 
 
 def say(*a):
@@ -46,8 +56,13 @@ def inputs(seed=11):
     return G, M, W
 
 
-def plans(G, W):
+def plans(G, W, check_routes=False):
     fused = d.plan_for(G, [w.dtype for w in W])
+    if check_routes:
+        for i, (r, c, pd) in enumerate(SHAPES):
+            resident = fused.bucket(fused.query(i).bucket).resident
+            assert resident == ((r, c, pd) in RESIDENT), (r, c, pd)
+            assert fused.update_fused(i) == (resident or (pd == "bf16" and c % 8 == 0)), (r, c, pd)
     entries = []
     for b in range(fused.info()[1]):
         e = fused.config(b)
@@ -66,7 +81,7 @@ def bits(t):
 @pytest.mark.parametrize("steps", [5, 1, 2])
 def test_fused_update_matches_the_apply_pass_bitwise(steps):
     G, M0, W0 = inputs()
-    fused, separate = plans(G, W0)
+    fused, separate = plans(G, W0, check_routes=True)
     out = {}
     for name, plan in (("fused", fused), ("separate", separate)):
         say(f"case fused update: step, {name} plan, ns_steps {steps}")
