@@ -537,6 +537,12 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
             }
         };
         auto inside = [&](int64_t prow, int64_t pcol) { return prow < rows && pcol < cols; };
+        // The W loads are unconditional (a chunk outside the matrix reads the
+        // first one and is never stored) and each w[u] is marked used on every
+        // path where the update consumes it: a load left pending on some path
+        // of the tile loop made the compiler wait for all memory traffic
+        // before every later load into the same registers, so the 16 loads of
+        // a piece went out one round trip at a time.
         u32x4_t w[kUpd];
         auto load_w = [&](int h) {
             if (!args.update) return;
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 int64_t prow, pcol;
                 int er, ec;
                 chunk(h, u, prow, pcol, er, ec);
-                if (inside(prow, pcol)) w[u] = ld_stream<u32x4_t>(W + prow * cols + pcol);
+                w[u] = ld_stream<u32x4_t>(W + (inside(prow, pcol) ? prow * cols + pcol : 0));
             }
         };
         auto update = [&](int h) {
@@ -554,6 +560,7 @@ __global__ __launch_bounds__(TileCfg<T>::NT, 1) void ns_gemm_bf16_kernel(GemmArg
                 int64_t prow, pcol;
                 int er, ec;
                 chunk(h, u, prow, pcol, er, ec);
+                if (args.update) asm volatile("" : "+v"(w[u]));
                 u32x4_t o;
                 if (!tall) {
                     o = *reinterpret_cast<const u32x4_t*>(erow(ebuf, er) + (((ec >> 3) ^ swizzle_e<T>(er)) << 4));
