@@ -3,7 +3,11 @@
 // n_pad bf16, up to 128 KB) and the 128 x 128 A / B' array (32 KB) stay in
 // LDS, so an iteration costs three barriers instead of three grouped launches.
 // Launches of such single-tile products are latency-bound (a few microseconds
-// each, whatever their size), which is what this kernel removes.
+// each, whatever their size), which is what this kernel removes.  It also
+// takes over the per-matrix launches around the iteration: it sums the
+// matrix's norm partials itself and, on the default route, writes the
+// parameter update (or the output) from the final X in LDS, so neither the
+// finalize nor the apply pass runs for its matrices.
 //
 // The arithmetic is the tiled kernels' short-side iteration, with the same
 // operand and output roundings: per iteration, with s = 1 / (||U||_F + eps) in
